@@ -1,0 +1,336 @@
+"""fp64 oracle of the FP8 P-cast attention forward (online softmax, block order, S).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What it computes, and where the pages fix it
+--------------------------------------------
+P-Cast technical summary ("P-Cast Precision in FP8 Attention", gist.science):
+  * §1 Problem statement: Q·K^T and P·V run on FP8 (E4M3) operands; the softmax
+    probabilities P are cast to E4M3 before the P·V product; an online softmax keeps a
+    running maximum m over the KV blocks, so a large sink logit raises m and pushes the
+    later non-sink P towards zero ("P-collapse").
+  * §1, the two implementation choices: the KV block order (forward 0->N or reverse
+    N->0) and a static scale S multiplied onto P before the cast and divided back out
+    in the epilogue.
+  * §2 Optimization 2, condition 1: for S = 2^k the multiply and divide are exact.
+EFQ-Softmax abstract ("EFQ-Softmax: Exp-Free Quantization for Softmax"): the
+conventional low-bit path evaluates the shifted exponentials in high precision, forms
+the probability block, then quantizes it for the low-bit P·V product; the row-max
+update, the rescale of the history, high-precision accumulation and the final
+normalisation are the usual FlashAttention steps.
+
+Readings taken where the pages leave a step open (each is listed in the design notes):
+  * the logits are natural-log units with the usual 1/sqrt(d) scale;
+  * KV blocks are 64 keys wide, aligned at key 0; the running max is updated exactly
+    once per block, starting from -inf;
+  * the row sum l accumulates the *unquantized* P~ = exp(s - m); only the operand of
+    P·V is scaled and cast (the pages apply S and the cast "before the P·V product");
+  * the cast is E4M3FN round-to-nearest-even of the fp64 product P~·S;
+  * O = acc / (S·l) once, in the epilogue;
+  * causal masking is j <= i with equal query and key lengths; a block that is
+    entirely masked for a row leaves that row's state unchanged.
+
+Everything is fp64. Q·K^T is taken over the raw decoded E4M3 values, which is exact
+in fp64 (every product is a multiple of 2^-18 and every partial sum stays far below
+2^53 of those units), and the descales are applied afterwards.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import e4m3
+
+BLOCK = 64
+N_SINK_DEFAULT = 4
+FLIP_REL_WINDOW = 2.0 ** -16      # relative half-width of the rounding-boundary band
+
+
+# --------------------------------------------------------------------------------------
+# inputs
+# --------------------------------------------------------------------------------------
+
+def head_logits_e4m3(q8, k8, qd: float, kd: float, d: int, rows=None, causal=False):
+    """Natural-log logits s = (dec(Q8)·dec(K8)^T)·qd·kd/sqrt(d) for one head, fp64.
+
+    ``q8``: [N, d] uint8, ``k8``: [N, d] uint8. ``rows``: optional query row indices.
+    Masked entries (causal, j > i) are -inf.
+    """
+    qv = e4m3.decode(q8)
+    kv = e4m3.decode(k8)
+    idx = np.arange(qv.shape[0]) if rows is None else np.asarray(rows)
+    raw = qv[idx] @ kv.T                        # exact: see module docstring
+    s = raw * (float(qd) * float(kd)) / math.sqrt(d)
+    if causal:
+        s = np.where(np.arange(kv.shape[0])[None, :] > idx[:, None], -np.inf, s)
+    return s, idx
+
+
+def head_logits_float(q, k, d: int, rows=None, causal=False):
+    """Logits from real-valued Q, K (the "Q, K, V kept in fp32" simulation mode)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = (q[idx] @ k.T) / math.sqrt(d)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > idx[:, None], -np.inf, s)
+    return s, idx
+
+
+def block_visit_order(n_keys: int, kv_order: str, block: int = BLOCK):
+    """Block indices in visit order: forward 0..nb-1 or reverse nb-1..0.
+
+    With causal masking a block past a row's diagonal is fully masked for that row
+    and is a no-op, so row i effectively visits 0..floor(i/64) (forward) or
+    floor(i/64)..0 (reverse): the reverse walk starts at the diagonal block.
+    """
+    nb = n_keys // block
+    if kv_order == "forward":
+        return list(range(nb))
+    if kv_order == "reverse":
+        return list(range(nb - 1, -1, -1))
+    raise ValueError(kv_order)
+
+
+# --------------------------------------------------------------------------------------
+# the online-softmax P-cast forward, block by block (the method's own order)
+# --------------------------------------------------------------------------------------
+
+def _cast(p_scaled, p_cast: str):
+    if p_cast == "e4m3":
+        return e4m3.round_e4m3(p_scaled)
+    if p_cast == "bf16":
+        return e4m3.round_bf16(p_scaled)
+    if p_cast == "none":
+        return p_scaled
+    raise ValueError(p_cast)
+
+
+def online_softmax_pcast(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
+                         block: int = BLOCK, keep_trace: bool = False):
+    """Run the block-wise online softmax with the P-cast for a set of rows.
+
+    ``s``: [R, N] fp64 logits (-inf where masked). ``v``: [N, d] fp64 values (already
+    multiplied by their descale). For each row, blocks are visited in ``kv_order``;
+    per block:
+        m_new = max(m, max_j s_ij)
+        alpha = exp(m - m_new)                     (0 while m = -inf)
+        P~_ij = exp(s_ij - m_new)
+        P8_ij = cast(P~_ij · S)
+        l     = alpha·l + sum_j P~_ij              (unquantized P~)
+        acc   = alpha·acc + sum_j P8_ij · v_j
+        m     = m_new
+    and O = acc / (S·l). Rows are processed together but every row follows exactly
+    its own sequence; a block with no unmasked key for a row changes nothing for it.
+
+    Returns (O [R, d], trace) where ``trace`` (if requested) holds, per visited block,
+    the block index, m after the block, P~ and the cast operand P8.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    R, N = s.shape
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, v.shape[1]))
+    trace = []
+    for b in block_visit_order(N, kv_order, block):
+        sb = s[:, b * block:(b + 1) * block]
+        live = np.isfinite(sb)                               # unmasked entries
+        row_live = live.any(axis=1)
+        bmax = np.where(live, sb, -np.inf).max(axis=1)
+        m_new = np.where(row_live, np.maximum(m, bmax), m)
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+            p = np.where(live, np.exp(sb - m_new[:, None]), 0.0)
+        p8 = _cast(p * S, p_cast)
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p8 @ v[b * block:(b + 1) * block]
+        m = m_new
+        if keep_trace:
+            trace.append({"block": b, "m": m.copy(), "p": p, "p8": p8, "live": live})
+    o = acc / (S * l[:, None])
+    return o, trace
+
+
+def online_softmax_pcast_vectorized(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
+                                    block: int = BLOCK):
+    """The same result written in closed form instead of as a recurrence.
+
+    Let m_b(i) be row i's running max right after visiting block b and m_f(i) the final
+    max. Unrolling the recurrence, block b's contribution is rescaled by every later
+    alpha, i.e. by exp(m_b - m_f), and the row sum telescopes to sum_j exp(s_ij - m_f):
+
+        O_i = sum_j cast(exp(s_ij - m_b(j)(i))·S)·exp(m_b(j)(i) - m_f(i))·v_j
+              / (S · sum_j exp(s_ij - m_f(i)))
+
+    where b(j) is the block of key j. Equal to the recurrence in real arithmetic.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    R, N = s.shape
+    order = block_visit_order(N, kv_order, block)
+    nb = N // block
+    bmax = np.where(np.isfinite(s), s, -np.inf).reshape(R, nb, block).max(axis=2)   # [R, nb]
+    run = np.full((R, nb), -np.inf)
+    cur = np.full(R, -np.inf)
+    for b in order:
+        cur = np.maximum(cur, bmax[:, b])
+        run[:, b] = cur
+    m_f = cur
+    m_at_key = np.repeat(run, block, axis=1)                                       # [R, N]
+    live = np.isfinite(s)
+    with np.errstate(invalid="ignore"):
+        p = np.where(live, np.exp(s - m_at_key), 0.0)
+        w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
+        l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1)
+    p8 = _cast(p * S, p_cast)
+    return ((p8 * w) @ np.asarray(v, dtype=np.float64)) / (S * l[:, None])
+
+
+def exact_attention(s, v):
+    """Plain softmax(s)·v in fp64 (no cast): the exact attention the cast perturbs."""
+    s = np.asarray(s, dtype=np.float64)
+    mx = np.where(np.isfinite(s), s, -np.inf).max(axis=1, keepdims=True)
+    e = np.where(np.isfinite(s), np.exp(s - mx), 0.0)
+    return (e / e.sum(axis=1, keepdims=True)) @ np.asarray(v, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# P-collapse diagnostic
+# --------------------------------------------------------------------------------------
+
+def collapse_counts(s, *, kv_order: str, S: float, n_sink: int = N_SINK_DEFAULT,
+                    block: int = BLOCK, row_ids=None):
+    """Counts of collapsed non-sink probabilities for a set of rows.
+
+    A probability collapses when its cast operand is the E4M3 zero although the key is
+    unmasked (P-Cast summary, §1: non-sink P underflows to zero under the inflated
+    running max). Only non-sink keys j >= n_sink are counted. Returns a length-4
+    integer vector:
+        [0] collapsed non-sink P over all blocks
+        [1] of which in blocks that contain a sink key (64·b < n_sink)
+        [2] unmasked non-sink (i, j) pairs over all blocks
+        [3] of which in blocks that contain a sink key
+    The cast operand is computed exactly as in ``online_softmax_pcast``.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    R, N = s.shape
+    out = np.zeros(4, dtype=np.int64)
+    m = np.full(R, -np.inf)
+    keys = np.arange(N)
+    for b in block_visit_order(N, kv_order, block):
+        sb = s[:, b * block:(b + 1) * block]
+        live = np.isfinite(sb)
+        row_live = live.any(axis=1)
+        bmax = np.where(live, sb, -np.inf).max(axis=1)
+        m = np.where(row_live, np.maximum(m, bmax), m)
+        with np.errstate(invalid="ignore"):
+            p = np.where(live, np.exp(sb - m[:, None]), 0.0)
+        code = e4m3.encode(p * S)
+        nonsink = (keys[b * block:(b + 1) * block] >= n_sink)[None, :]
+        counted = live & nonsink
+        zero = counted & (code == 0)
+        sink_block = b * block < n_sink
+        out[0] += int(zero.sum())
+        out[2] += int(counted.sum())
+        if sink_block:
+            out[1] += int(zero.sum())
+            out[3] += int(counted.sum())
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# rounding-boundary allowance
+# --------------------------------------------------------------------------------------
+
+def _e4m3_boundaries():
+    vals = e4m3.all_finite_values()
+    mids = (vals[:-1] + vals[1:]) / 2.0          # rounding midpoints; mids[0] = 2^-10
+    steps = vals[1:] - vals[:-1]
+    return mids, steps
+
+
+def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK):
+    """Per-element extra tolerance for cast operands that sit on a rounding boundary.
+
+    A device computing P~·S in fp32 (with its own exp) and this fp64 oracle may round a
+    value lying within a relative ``FLIP_REL_WINDOW`` of an E4M3 rounding midpoint to
+    the two neighbouring codes; both are correct roundings of the respective inputs.
+    For each such (i, j) the output row may move by step/S·exp(m_b - m_f)·|v_j|/l.
+    Returns (allow [R, d], flagged [R, N] bool, zero_flagged [R] int: flagged pairs at
+    the 0 / 2^-9 boundary, which can move the collapse count).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    R, N = s.shape
+    mids, steps = _e4m3_boundaries()
+    nb = N // block
+    order = block_visit_order(N, kv_order, block)
+    bmax = np.where(np.isfinite(s), s, -np.inf).reshape(R, nb, block).max(axis=2)
+    run = np.full((R, nb), -np.inf)
+    cur = np.full(R, -np.inf)
+    for b in order:
+        cur = np.maximum(cur, bmax[:, b])
+        run[:, b] = cur
+    m_f = cur
+    m_at_key = np.repeat(run, block, axis=1)
+    live = np.isfinite(s)
+    with np.errstate(invalid="ignore"):
+        x = np.where(live, np.exp(s - m_at_key) * S, 0.0)
+        w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
+        l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1)
+    k = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
+    # nearest midpoint is mids[k-1] or mids[k]
+    lo, hi = mids[k - 1], mids[k]
+    near_lo = np.abs(x - lo) <= FLIP_REL_WINDOW * lo
+    near_hi = np.abs(x - hi) <= FLIP_REL_WINDOW * hi
+    step = np.where(near_lo, steps[k - 1], np.where(near_hi, steps[k], 0.0))
+    flagged = live & (near_lo | near_hi)
+    zero_flag = live & ((near_lo & (k - 1 == 0)) | (near_hi & (k == 0)))
+    weight = np.where(flagged, step * w, 0.0) / (S * l[:, None])
+    allow = weight @ v
+    return allow, flagged, zero_flag.sum(axis=1)
+
+
+# --------------------------------------------------------------------------------------
+# whole-tensor driver
+# --------------------------------------------------------------------------------------
+
+def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str,
+                   S: float, rows=None, heads=None, n_sink: int = N_SINK_DEFAULT,
+                   with_allowance: bool = False, with_counts: bool = False):
+    """Oracle over [B, H, N, d] E4M3 inputs (GQA: query head h reads kv head h // (H/Hkv)).
+
+    ``q_descale`` is [B, H], ``k_descale``/``v_descale`` are [B, Hkv]. ``rows`` limits the
+    query rows (same subset for every head); ``heads`` is an optional list of (b, h).
+    Returns dict with ``o`` [len(heads), R, d], ``rows``, ``heads`` and, if asked,
+    ``allow`` (same shape as o), ``zero_flagged`` and ``counts`` (summed over heads).
+    """
+    B, H, N, d = q8.shape
+    Hkv = k8.shape[1]
+    group = H // Hkv
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    outs, allows, zflag = [], [], 0
+    counts = np.zeros(4, dtype=np.int64)
+    idx = None
+    for (b, h) in heads:
+        hk = h // group
+        s, idx = head_logits_e4m3(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                  rows=rows, causal=causal)
+        vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
+        o, _ = online_softmax_pcast(s, vf, kv_order=kv_order, S=S)
+        outs.append(o)
+        if with_allowance:
+            a, _, z = flip_allowance(s, vf, kv_order=kv_order, S=S)
+            allows.append(a)
+            zflag += int(z.sum())
+        if with_counts:
+            counts += collapse_counts(s, kv_order=kv_order, S=S, n_sink=n_sink)
+    res = {"o": np.stack(outs), "rows": idx, "heads": heads}
+    if with_allowance:
+        res["allow"] = np.stack(allows)
+        res["zero_flagged"] = zflag
+    if with_counts:
+        res["counts"] = counts
+    return res

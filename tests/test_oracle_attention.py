@@ -1,0 +1,284 @@
+"""Pins of the attention oracle (CPU only).
+
+Each check ties the oracle to something other than itself: the textbook softmax, a
+closed-form special case worked by hand, an independent pure-Python brute force, exact
+rational arithmetic, or the statistics the P-Cast pages print.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from oracle import attention as A
+from oracle import e4m3, theory
+from precision_attention_amd import inputs as I
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")))
+
+
+def _rand_logits(R, N, seed, scale=2.0, causal=False, sink=None):
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((R, N)) * scale
+    if sink is not None:
+        s[:, :4] += sink
+    if causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(R)[:, None], -np.inf, s)
+    return s
+
+
+# ------------------------------------------------------------------ exact special cases
+
+@pytest.mark.parametrize("order", ["forward", "reverse"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_without_cast_equals_textbook_softmax(order, causal):
+    s = _rand_logits(192, 192, 3, causal=causal)
+    v = np.random.default_rng(4).standard_normal((192, 16))
+    o, _ = A.online_softmax_pcast(s, v, kv_order=order, S=256.0, p_cast="none")
+    ref = softmax(s, axis=1) @ v
+    assert np.abs(o - ref).max() < 1e-12
+    assert np.abs(A.exact_attention(s, v) - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("S", [1.0, 16.0, 256.0, 448.0])
+def test_uniform_logits_give_mean_of_v(S):
+    # every P~ is 1, P·S = S is an E4M3 value, so O is the plain mean of V
+    s = np.zeros((3, 256))
+    v = np.random.default_rng(5).standard_normal((256, 8))
+    for order in ("forward", "reverse"):
+        o, _ = A.online_softmax_pcast(s, v, kv_order=order, S=S)
+        assert np.abs(o - v.mean(axis=0)).max() < 1e-14
+
+
+def test_single_sink_hand_worked():
+    """One row, two 64-key blocks, key 0 has logit Δ = 8, the other 127 keys logit 0.
+
+    Forward, S = 1: block 0 sets m = 8 and every non-sink P~ = e^-8 = 3.4e-4 <= 2^-10
+    casts to 0, so only the sink reaches P·V: O = v0 / (1 + 127 e^-8).
+    Reverse, S = 1: block 1 first with m = 0 (P~ = 1, cast exact); then block 0 raises m
+    to 8, rescales by e^-8 and its 63 non-sink P~ = e^-8 cast to 0:
+    O = (e^-8·sum_{j>=64} v_j + v0) / (1 + 127 e^-8).
+    Forward, S = 256: e^-8·256 = 0.08588 lies in [2^-4, 2^-3) with step 2^-7 and
+    rounds to 11·2^-7 = 0.0859375: O = (256 v0 + 0.0859375 sum_{j>=1} v_j) / (256 (1 + 127 e^-8)).
+    """
+    s = np.zeros((1, 128))
+    s[0, 0] = 8.0
+    v = np.random.default_rng(6).standard_normal((128, 4))
+    l = 1 + 127 * math.exp(-8)
+    o, _ = A.online_softmax_pcast(s, v, kv_order="forward", S=1.0)
+    assert np.abs(o[0] - v[0] / l).max() < 1e-14
+    o, _ = A.online_softmax_pcast(s, v, kv_order="reverse", S=1.0)
+    assert np.abs(o[0] - (math.exp(-8) * v[64:].sum(0) + v[0]) / l).max() < 1e-14
+    assert e4m3.round_e4m3(256 * math.exp(-8)) == 0.0859375
+    o, _ = A.online_softmax_pcast(s, v, kv_order="forward", S=256.0)
+    assert np.abs(o[0] - (256 * v[0] + 0.0859375 * v[1:].sum(0)) / (256 * l)).max() < 1e-14
+    # counts with key 0 as the only sink
+    c = A.collapse_counts(s, kv_order="forward", S=1.0, n_sink=1)
+    assert list(c) == [127, 63, 127, 63]
+    c = A.collapse_counts(s, kv_order="reverse", S=1.0, n_sink=1)
+    assert list(c) == [63, 63, 127, 63]
+    c = A.collapse_counts(s, kv_order="forward", S=256.0, n_sink=1)
+    assert list(c) == [0, 0, 127, 63]
+
+
+def test_logits_exact_over_decoded_e4m3():
+    inp = I.make_inputs(1, 1, 1, 64, 64, delta=8.0, seed=7, descale="tensor")
+    q8, k8 = inp["q8"][0, 0], inp["k8"][0, 0]
+    s, _ = A.head_logits_e4m3(q8, k8, 1.0, 1.0, 64)
+    dec = {c: Fraction(float(e4m3.decode(np.uint8(c)))) for c in range(256) if (c & 0x7F) != 0x7F}
+    for i, j in [(0, 0), (5, 9), (63, 1), (17, 40)]:
+        exact = sum(dec[int(a)] * dec[int(b)] for a, b in zip(q8[i], k8[j]))
+        assert Fraction(s[i, j] * 8.0) == exact          # sqrt(64) = 8: exact scaling
+
+
+# ------------------------------------------------------------------ independent formulations
+
+def _nearest_e4m3_scalar(x):
+    """Nearest finite E4M3 value by scanning the table (ties -> even code), saturating."""
+    if x >= 448.0:
+        return 448.0
+    best = None
+    for code, val in enumerate(e4m3.all_finite_values()):
+        dist = abs(val - x)
+        if best is None or dist < best[0] or (dist == best[0] and code % 2 == 0):
+            best = (dist, val)
+    return best[1]
+
+
+def _brute_force_row(s_row, v, order, S):
+    N, d = v.shape
+    blocks = range(N // 64) if order == "forward" else range(N // 64 - 1, -1, -1)
+    m, l, acc = -math.inf, 0.0, [0.0] * d
+    for b in blocks:
+        keys = [j for j in range(64 * b, 64 * b + 64) if s_row[j] != -math.inf]
+        if not keys:
+            continue
+        m_new = max(m, max(s_row[j] for j in keys))
+        alpha = 0.0 if m == -math.inf else math.exp(m - m_new)
+        l *= alpha
+        acc = [a * alpha for a in acc]
+        for j in keys:
+            p = math.exp(s_row[j] - m_new)
+            l += p
+            p8 = _nearest_e4m3_scalar(p * S)
+            for c in range(d):
+                acc[c] += p8 * v[j, c]
+        m = m_new
+    return [a / (S * l) for a in acc]
+
+
+@pytest.mark.parametrize("order,S,causal", [("forward", 1.0, False), ("reverse", 256.0, True),
+                                            ("forward", 448.0, True), ("reverse", 16.0, False)])
+def test_brute_force_python_loops(order, S, causal):
+    s = _rand_logits(24, 128, 8, scale=2.5, causal=causal, sink=6.0)
+    v = np.random.default_rng(9).standard_normal((128, 5))
+    o, _ = A.online_softmax_pcast(s, v, kv_order=order, S=S)
+    for i in range(s.shape[0]):
+        ref = _brute_force_row(s[i], v, order, S)
+        assert np.abs(o[i] - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("order", ["forward", "reverse"])
+@pytest.mark.parametrize("S", [1.0, 256.0, 448.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sequential_equals_closed_form(order, S, causal):
+    s = _rand_logits(256, 512, 11, scale=1.5, causal=causal, sink=9.0)
+    v = np.random.default_rng(12).standard_normal((512, 16))
+    o, _ = A.online_softmax_pcast(s, v, kv_order=order, S=S)
+    ov = A.online_softmax_pcast_vectorized(s, v, kv_order=order, S=S)
+    assert np.abs(o - ov).max() < 1e-12
+
+
+def test_reverse_causal_starts_at_diagonal_block():
+    s = _rand_logits(256, 256, 13, causal=True)
+    v = np.ones((256, 2))
+    _, trace = A.online_softmax_pcast(s, v, kv_order="reverse", S=256.0, keep_trace=True)
+    first = np.full(256, -1)
+    for step in trace:
+        newly = (first < 0) & step["live"].any(axis=1)
+        first[newly] = step["block"]
+    assert (first == np.arange(256) // 64).all()
+
+
+def test_gqa_head_mapping():
+    inp = I.make_inputs(1, 4, 2, 128, 64, delta=4.0, seed=14)
+    res = A.attention_e4m3(inp["q8"], inp["k8"], inp["v8"], inp["qd"], inp["kd"], inp["vd"],
+                           causal=True, kv_order="reverse", S=256.0)
+    for h in range(4):
+        hk = h // 2
+        s, _ = A.head_logits_e4m3(inp["q8"][0, h], inp["k8"][0, hk], inp["qd"][0, h], inp["kd"][0, hk], 64, causal=True)
+        vf = e4m3.decode(inp["v8"][0, hk]) * float(inp["vd"][0, hk])
+        o, _ = A.online_softmax_pcast(s, vf, kv_order="reverse", S=256.0)
+        assert np.array_equal(res["o"][h], o)
+
+
+def test_flip_allowance_hand_case():
+    # P~·S sits 2^-20 (relative) above the 2^-10 zero boundary: flagged, allowance 2^-9·|v1|/l
+    s = np.full((1, 64), -np.inf)
+    s[0, 0] = 0.0
+    s[0, 1] = math.log(2.0 ** -10 * (1 + 2.0 ** -20))
+    v = np.zeros((64, 2))
+    v[1] = [3.0, -5.0]
+    allow, flagged, zf = A.flip_allowance(s, v, kv_order="forward", S=1.0)
+    l = 1 + 2.0 ** -10 * (1 + 2.0 ** -20)
+    assert flagged[0, 1] and not flagged[0, 0] and zf[0] == 1
+    assert np.allclose(allow[0], [2.0 ** -9 * 3.0 / l, 2.0 ** -9 * 5.0 / l], rtol=1e-12)
+
+
+# ------------------------------------------------------------------ the pages' statistics
+
+@pytest.fixture(scope="module")
+def sweep_logits():
+    """One head of the Δ sweep (N = 4096, d = 128, clean sinks, per-tensor E4M3)."""
+    out = {}
+    for delta in (6.0, 7.0, 8.0, 10.0, 12.0):
+        inp = I.make_inputs(1, 1, 1, 4096, 128, delta=delta, seed=0, descale="tensor", keep_float=False)
+        s, _ = A.head_logits_e4m3(inp["q8"][0, 0], inp["k8"][0, 0], inp["qd"][0, 0], inp["kd"][0, 0], 128)
+        out[delta] = s
+    return out
+
+
+def _probit(p):
+    from scipy.stats import norm
+    return norm.ppf(p)
+
+
+@pytest.mark.parametrize("delta,S", [(6.0, 1.0), (7.0, 1.0), (8.0, 16.0), (10.0, 16.0),
+                                     (10.0, 256.0), (12.0, 256.0), (12.0, 448.0)])
+def test_forward_collapse_fraction_vs_closed_form(sweep_logits, delta, S):
+    s = sweep_logits[delta]
+    c = A.collapse_counts(s, kv_order="forward", S=S)
+    f_meas = c[0] / c[2]
+    f_print = float(theory.collapse_fraction(delta, S))
+    assert abs(_probit(f_meas) - _probit(f_print)) <= 1.0, (f_meas, f_print)
+    # per-row form of the same tail (realised sink-block max, row's own non-sink law)
+    mx = s[:, :64].max(axis=1)
+    ns = s[:, 4:]
+    f_row = theory.collapse_fraction_rowwise(mx, ns.mean(axis=1), ns.std(axis=1), S)
+    assert abs(f_meas / f_row - 1) < 0.15, (f_meas, f_row)
+
+
+def test_threshold_brackets(sweep_logits):
+    """Δ_c = 6.93 + ln S - δ_k: F crosses 1/2 between the bracketing sweep values."""
+    def frac(delta, S):
+        c = A.collapse_counts(sweep_logits[delta], kv_order="forward", S=S)
+        return c[0] / c[2]
+    assert frac(6.0, 1.0) > 0.5 > (theory.collapse_fraction(4.0, 1.0))
+    assert theory.collapse_threshold(1.0) < 6.0
+    assert frac(8.0, 16.0) < 0.5 < frac(10.0, 16.0)
+    assert frac(10.0, 256.0) < 0.5 < frac(12.0, 256.0)
+    assert abs(frac(12.0, 448.0) - 0.5) < 0.05
+
+
+@pytest.mark.parametrize("delta", [7.0, 8.0, 10.0, 12.0])
+def test_reverse_s256_no_collapse_before_sink_block(sweep_logits, delta):
+    c = A.collapse_counts(sweep_logits[delta], kv_order="reverse", S=256.0)
+    assert c[0] - c[1] == 0
+    # the sink block's co-resident keys still see the sink max, as under forward order
+    cf = A.collapse_counts(sweep_logits[delta], kv_order="forward", S=256.0)
+    assert c[1] == cf[1]
+
+
+def _mse_pcast(n, delta, configs, seed=0):
+    """MSE of the P-cast output against exact attention with Q, K, V kept in fp32."""
+    inp = I.make_inputs(1, 1, 1, n, 128, delta=delta, seed=seed, descale="tensor")
+    q, k, v = (inp[x][0, 0].astype(np.float64) for x in ("q", "k", "v"))
+    s, _ = A.head_logits_float(q, k, 128)
+    ex = A.exact_attention(s, v)
+    out = {}
+    for order, S in configs:
+        o, _ = A.online_softmax_pcast(s, v, kv_order=order, S=S)
+        out[(order, S)] = float(np.mean((o - ex) ** 2))
+    return out
+
+
+def test_mse_ratios_match_printed_ranges():
+    mse = _mse_pcast(4096, 7.0, [("forward", 1.0), ("reverse", 256.0), ("forward", 256.0)])
+    lo, hi = GOLD["mse_ratio_forward_s1_vs_optimised"]["value"]
+    r = mse[("forward", 1.0)] / mse[("reverse", 256.0)]
+    assert lo <= r <= hi, r
+    # saturation: reverse+256 indistinguishable from forward+256
+    assert abs(mse[("reverse", 256.0)] / mse[("forward", 256.0)] - 1.0) < 0.02
+
+
+@pytest.mark.parametrize("delta", [7.0, 8.0, 10.0])
+def test_s256_beats_s448_forward(delta):
+    """Printed: forward S=256 has lower MSE than forward S=448 (d_p is 14% larger at 448).
+    The printed size of the gain (10-15%) belongs to the pages' own P distribution, which
+    they do not give; on this synthetic recipe the gain is a few percent. The direction is
+    pinned, the size is reported."""
+    mse = _mse_pcast(4096, delta, [("forward", 256.0), ("forward", 448.0)])
+    g = mse[("forward", 448.0)] / mse[("forward", 256.0)] - 1.0
+    assert 0.0 < g < 0.20, g
+
+
+def test_mse_gain_grows_with_sequence_length():
+    cfg = [("forward", 1.0), ("reverse", 256.0)]
+    r = []
+    for n in (512, 1024, 4096):
+        m = _mse_pcast(n, 7.0, cfg)
+        r.append(m[cfg[0]] / m[cfg[1]])
+    assert r[0] < r[1] < r[2], r
