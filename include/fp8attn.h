@@ -1,0 +1,99 @@
+/*
+ * fp8attn.h -- C ABI of the MI355X (gfx950) FP8 P-cast attention forward.
+ *
+ * The operation. Attention O = softmax(Q K^T / sqrt(d)) V computed block-wise with an
+ * online softmax, where Q, K, V are OCP E4M3 ("e4m3fn") codes with fp32 descales, and
+ * the probability tile P~ = exp(s - m) is multiplied by a static scale S and cast to
+ * E4M3 before the P.V product; S is divided back out in the epilogue. The KV blocks
+ * (64 keys each, aligned at key 0) are visited in forward (0 -> N) or reverse (N -> 0)
+ * order; the running max m is updated once per block. This is the computation analysed
+ * in "P-Cast Precision in FP8 Attention: Sink-Induced Collapse and the Optimality of
+ * S=2^8" (gist.science technical summary, section 1 "Problem statement": P cast to E4M3
+ * before P.V, the running max m, the KV block order and the static scale S; section 2
+ * "Optimization 2", condition 1: S = 2^k makes the scale and its inverse exact).
+ *
+ * Per query row i (natural-log logits s_ij = (q_i . k_j) qd kd / sqrt(d)):
+ *   for each visited block b:  m' = max(m, max_j s_ij);  a = exp(m - m');
+ *                              P~_ij = exp(s_ij - m');    P8_ij = E4M3_RNE(P~_ij * S);
+ *                              l = a l + sum_j P~_ij;     acc = a acc + sum_j P8_ij v_j;
+ *   O_i = acc / (S l)
+ * The row sum uses the unquantized P~. The kernel evaluates exponentials as exp2 of
+ * log2(e)-scaled logits in fp32, accumulates both GEMMs in fp32 on the FP8 matrix
+ * cores, and for S = 2^k applies the scale as an exponent offset (exact).
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or retains them. Tensors are dense, row-major, 16-byte aligned:
+ *      q  [B][H][N][d]   uint8 E4M3 codes      o [B][H][N][d] float32 (written)
+ *      k  [B][Hkv][N][d] uint8 E4M3 codes      v [B][Hkv][N][d] uint8 E4M3 codes
+ *      q_descale [B*H], k_descale [B*Hkv], v_descale [B*Hkv] float32, each > 0 and
+ *      finite (decoded value = code value * descale; per-tensor = the same value repeated).
+ *  - Grouped-query attention: query head h reads kv head h / (H / Hkv).
+ *  - causal != 0 masks key j > query i (equal query and key lengths).
+ *  - kv_order: FP8ATTN_KV_FORWARD (0) or FP8ATTN_KV_REVERSE (1).
+ *  - 0 < S <= 448 (the E4M3 maximum; P~ <= 1 so P~ S never overflows). S = 2^k is exact;
+ *    other values are accepted and round like any fp32 multiply.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream). Calls are
+ *    asynchronous: they enqueue kernels and return; no host synchronisation.
+ *  - Errors: every argument is validated BEFORE any HIP call; on a negative status
+ *    nothing has been launched and no memory was touched. FP8ATTN_ELAUNCH reports the
+ *    HIP error recorded right after the launch. Device-side faults (bad pointers) are
+ *    reported by HIP on later calls, as for any kernel.
+ *  - NaN codes (0x7F / 0xFF) or non-finite descales propagate NaN into O; not detected.
+ *  - No global state, thread-safe, no exceptions cross the ABI.
+ */
+#ifndef FP8ATTN_H
+#define FP8ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8ATTN_OK = 0,
+  FP8ATTN_EINVAL = -1,       /* null pointer, size <= 0, H % Hkv != 0, S not in (0,448],
+                                kv_order/causal not 0/1, n_sink out of [0, N] */
+  FP8ATTN_EUNSUPPORTED = -2, /* d not in {64,128,256}, N % 64 != 0, pointer not 16-byte
+                                aligned, grid larger than 2^31-1 workgroups */
+  FP8ATTN_ELAUNCH = -3       /* HIP reported an error for the launch */
+} fp8attn_status;
+
+enum { FP8ATTN_KV_FORWARD = 0, FP8ATTN_KV_REVERSE = 1 };
+
+/* The forward pass: writes o (every element of [B][H][N][d]). */
+int fp8_attn_fwd(const void* q, const void* k, const void* v, float* o,
+                 int B, int H, int Hkv, int N, int d,
+                 int causal, int kv_order, float S,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 void* stream);
+
+/* P-collapse diagnostic: runs the same Q.K^T, running-max, exp and P~ S -> E4M3 path as
+ * fp8_attn_fwd (same block order and S; no P.V, no output) and counts, over unmasked
+ * pairs (i, j) with key j >= n_sink ("non-sink"), the cast operands that are the E4M3
+ * zero. A collapse is a non-sink probability that underflows to zero under the running
+ * max (technical summary, section 1; the fraction is the F(Delta, S) of section 2).
+ *   counts[0]  collapsed non-sink P, all blocks
+ *   counts[1]  of which in blocks that contain a sink key (64*b < n_sink)
+ *   counts[2]  unmasked non-sink pairs, all blocks
+ *   counts[3]  of which in blocks that contain a sink key
+ * counts: DEVICE pointer to 4 uint64, overwritten (zeroed on `stream` by a kernel, then
+ * accumulated with atomics). Read it after synchronising the stream. */
+int fp8_attn_p_collapse_count(const void* q, const void* k,
+                              int B, int H, int Hkv, int N, int d,
+                              int causal, int kv_order, float S,
+                              const float* q_descale, const float* k_descale,
+                              int n_sink, unsigned long long* counts, void* stream);
+
+/* Width in keys of the KV blocks between running-max updates (64). */
+int fp8_attn_kv_block(void);
+
+/* Library version string (static storage). */
+const char* fp8_attn_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp8_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8ATTN_H */

@@ -40,7 +40,7 @@ import math
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mfma_model
 
 BLOCK = 64
 N_SINK_DEFAULT = 4
@@ -246,50 +246,79 @@ def collapse_counts(s, *, kv_order: str, S: float, n_sink: int = N_SINK_DEFAULT,
 def _e4m3_boundaries():
     vals = e4m3.all_finite_values()
     mids = (vals[:-1] + vals[1:]) / 2.0          # rounding midpoints; mids[0] = 2^-10
-    steps = vals[1:] - vals[:-1]
-    return mids, steps
+    return vals, mids
 
 
-def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK):
-    """Per-element extra tolerance for cast operands that sit on a rounding boundary.
-
-    A device computing P~·S in fp32 (with its own exp) and this fp64 oracle may round a
-    value lying within a relative ``FLIP_REL_WINDOW`` of an E4M3 rounding midpoint to
-    the two neighbouring codes; both are correct roundings of the respective inputs.
-    For each such (i, j) the output row may move by step/S·exp(m_b - m_f)·|v_j|/l.
-    Returns (allow [R, d], flagged [R, N] bool, zero_flagged [R] int: flagged pairs at
-    the 0 / 2^-9 boundary, which can move the collapse count).
-    """
-    s = np.asarray(s, dtype=np.float64)
-    v = np.abs(np.asarray(v, dtype=np.float64))
+def _running_max_at_key(s, kv_order, block):
     R, N = s.shape
-    mids, steps = _e4m3_boundaries()
     nb = N // block
-    order = block_visit_order(N, kv_order, block)
     bmax = np.where(np.isfinite(s), s, -np.inf).reshape(R, nb, block).max(axis=2)
     run = np.full((R, nb), -np.inf)
     cur = np.full(R, -np.inf)
-    for b in order:
+    for b in block_visit_order(N, kv_order, block):
         cur = np.maximum(cur, bmax[:, b])
         run[:, b] = cur
-    m_f = cur
-    m_at_key = np.repeat(run, block, axis=1)
+    return np.repeat(run, block, axis=1), cur
+
+
+def _cast_operand(s, kv_order, S, block):
+    m_at_key, m_f = _running_max_at_key(s, kv_order, block)
     live = np.isfinite(s)
     with np.errstate(invalid="ignore"):
         x = np.where(live, np.exp(s - m_at_key) * S, 0.0)
+    return x, m_at_key, m_f, live
+
+
+def _codes_near(x, vals, mids):
+    """Nearest code of x and the code across the closest midpoint if x lies within the
+    relative window of that midpoint (else the same code)."""
+    code = e4m3.encode(x).astype(np.int64) & 0x7F
+    lo = np.clip(code - 1, 0, len(mids) - 1)
+    hi = np.clip(code, 0, len(mids) - 1)
+    near_lo = (code > 0) & (np.abs(x - mids[lo]) <= FLIP_REL_WINDOW * mids[lo])
+    near_hi = (code < len(vals) - 1) & (np.abs(x - mids[hi]) <= FLIP_REL_WINDOW * mids[hi])
+    other = np.where(near_lo, code - 1, np.where(near_hi, code + 1, code))
+    return code, other
+
+
+def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_device=None):
+    """Per-element extra tolerance where the device may legitimately pick another E4M3 code.
+
+    Two sources are covered. (1) A device evaluating P~·S in fp32 (its own exp) may round
+    a value lying within a relative ``FLIP_REL_WINDOW`` of a rounding midpoint to either
+    neighbour. (2) With ``s_device`` (logits as the device's matrix engine forms them, see
+    ``mfma_model``), the device's P~·S follows those logits and its running max, and may
+    land on a different code than the exact logits give.
+    For every (i, j) the set of admissible codes is: the exact code, the device-logit code,
+    and the neighbour across a midpoint within the window of either value. The allowance
+    of output (i, c) is sum_j max|admissible - exact code value|/S · exp(m_b - m_f) · |v_jc| / l.
+    Returns (allow [R, d], flagged [R, N] bool, zero_flagged [R] int: pairs whose admissible
+    codes include both zero and a nonzero code, which can move the collapse count).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    vals, mids = _e4m3_boundaries()
+    x, m_at_key, m_f, live = _cast_operand(s, kv_order, S, block)
+    c0, c1 = _codes_near(x, vals, mids)
+    cands = [c0, c1]
+    if s_device is not None:
+        xd, _, _, _ = _cast_operand(np.asarray(s_device, dtype=np.float64), kv_order, S, block)
+        d0, d1 = _codes_near(xd, vals, mids)
+        cands += [d0, d1]
+    dev = np.zeros_like(x)
+    has_zero = np.zeros(x.shape, dtype=bool)
+    has_nonzero = np.zeros(x.shape, dtype=bool)
+    for c in cands:
+        dev = np.maximum(dev, np.abs(vals[c] - vals[c0]))
+        has_zero |= c == 0
+        has_nonzero |= c != 0
+    flagged = live & (dev > 0)
+    zero_flag = live & has_zero & has_nonzero
+    with np.errstate(invalid="ignore"):
         w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
         l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1)
-    k = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)
-    # nearest midpoint is mids[k-1] or mids[k]
-    lo, hi = mids[k - 1], mids[k]
-    near_lo = np.abs(x - lo) <= FLIP_REL_WINDOW * lo
-    near_hi = np.abs(x - hi) <= FLIP_REL_WINDOW * hi
-    step = np.where(near_lo, steps[k - 1], np.where(near_hi, steps[k], 0.0))
-    flagged = live & (near_lo | near_hi)
-    zero_flag = live & ((near_lo & (k - 1 == 0)) | (near_hi & (k == 0)))
-    weight = np.where(flagged, step * w, 0.0) / (S * l[:, None])
-    allow = weight @ v
-    return allow, flagged, zero_flag.sum(axis=1)
+    weight = np.where(flagged, dev * w, 0.0) / (S * l[:, None])
+    return weight @ v, flagged, zero_flag.sum(axis=1)
 
 
 # --------------------------------------------------------------------------------------
@@ -297,15 +326,25 @@ def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK):
 # --------------------------------------------------------------------------------------
 
 def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str,
-                   S: float, rows=None, heads=None, n_sink: int = N_SINK_DEFAULT,
+                   S: float, rows=None, heads=None, n_sink: int = N_SINK_DEFAULT, logits: str = "exact",
                    with_allowance: bool = False, with_counts: bool = False):
     """Oracle over [B, H, N, d] E4M3 inputs (GQA: query head h reads kv head h // (H/Hkv)).
 
     ``q_descale`` is [B, H], ``k_descale``/``v_descale`` are [B, Hkv]. ``rows`` limits the
     query rows (same subset for every head); ``heads`` is an optional list of (b, h).
+
+    ``logits``: "exact" (the exact dot products of the decoded codes) or "device" (the
+    dot products as the gfx950 FP8 matrix core forms them, ``mfma_model``); the rest of
+    the algorithm is identical. ``with_allowance`` adds a per-element tolerance:
+      * for "device": only the fp32 rounding-boundary band around its own P~·S;
+      * for "exact": the codes the device may reach through its matrix-core logits (and the
+        band around both), plus |O(device logits) - O(exact logits)|, the continuous effect
+        of those logits on the row sum and rescaling.
     Returns dict with ``o`` [len(heads), R, d], ``rows``, ``heads`` and, if asked,
     ``allow`` (same shape as o), ``zero_flagged`` and ``counts`` (summed over heads).
     """
+    if logits not in ("exact", "device"):
+        raise ValueError(logits)
     B, H, N, d = q8.shape
     Hkv = k8.shape[1]
     group = H // Hkv
@@ -316,13 +355,23 @@ def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool,
     idx = None
     for (b, h) in heads:
         hk = h // group
-        s, idx = head_logits_e4m3(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
-                                  rows=rows, causal=causal)
+        s_exact, idx = head_logits_e4m3(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                        rows=rows, causal=causal)
+        s_dev = None
+        if logits == "device" or with_allowance:
+            s_dev = mfma_model.model_logits(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                            rows=rows, causal=causal)
+        s = s_exact if logits == "exact" else s_dev
         vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
         o, _ = online_softmax_pcast(s, vf, kv_order=kv_order, S=S)
         outs.append(o)
         if with_allowance:
-            a, _, z = flip_allowance(s, vf, kv_order=kv_order, S=S)
+            if logits == "device":
+                a, _, z = flip_allowance(s_dev, vf, kv_order=kv_order, S=S)
+            else:
+                a, _, z = flip_allowance(s_exact, vf, kv_order=kv_order, S=S, s_device=s_dev)
+                o_dev, _ = online_softmax_pcast(s_dev, vf, kv_order=kv_order, S=S)
+                a = a + np.abs(o_dev - o)
             allows.append(a)
             zflag += int(z.sum())
         if with_counts:

@@ -1,0 +1,147 @@
+"""Thin ctypes binding of the C ABI in include/fp8attn.h.
+
+Argument marshalling only: shape/dtype/device checks, output allocation through torch
+(device memory and streams are the only things torch provides), and a call into the
+HIP library. Every step of the attention runs in the library's kernels. There is no
+fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp8attn.so")
+
+FP8ATTN_OK = 0
+KV_ORDERS = {"forward": 0, "reverse": 1}
+
+_lib = None
+
+
+def _declare(lib):
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fp8_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp]
+    lib.fp8_attn_fwd.restype = i
+    lib.fp8_attn_p_collapse_count.argtypes = [vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp, vp]
+    lib.fp8_attn_p_collapse_count.restype = i
+    lib.fp8_attn_kv_block.argtypes = []
+    lib.fp8_attn_kv_block.restype = i
+    lib.fp8_attn_version.argtypes = []
+    lib.fp8_attn_version.restype = ctypes.c_char_p
+    lib.fp8_attn_status_string.argtypes = [i]
+    lib.fp8_attn_status_string.restype = ctypes.c_char_p
+
+
+def load():
+    """Load libfp8attn.so (built in-tree by ``build_lib.build()``); raise if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(LIB_PATH)
+        _declare(lib)
+        _lib = lib
+    return _lib
+
+
+def _status(rc: int, what: str):
+    if rc != FP8ATTN_OK:
+        msg = load().fp8_attn_status_string(rc).decode()
+        raise RuntimeError(f"{what} failed: status {rc} ({msg})")
+
+
+def _as_codes(t, name):
+    import torch
+
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name}: expected uint8 E4M3 codes or float8_e4m3fn, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    return t
+
+
+def _as_descale(t, n, name, device):
+    import torch
+
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name}: expected a contiguous float32 device tensor with {n} elements")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    return t
+
+
+def _shapes(q8, k8, v8=None):
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d] and [B, Hkv, N, d]")
+    B, H, N, d = q8.shape
+    Bk, Hkv, Nk, dk = k8.shape
+    if (Bk, Nk, dk) != (B, N, d):
+        raise ValueError(f"k shape {tuple(k8.shape)} does not match q {tuple(q8.shape)}")
+    if v8 is not None and tuple(v8.shape) != tuple(k8.shape):
+        raise ValueError(f"v shape {tuple(v8.shape)} differs from k {tuple(k8.shape)}")
+    return B, H, Hkv, N, d
+
+
+def _stream_ptr(device, stream):
+    import torch
+
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str = "reverse",
+        S: float = 256.0, out=None, stream=None):
+    """O = FP8 P-cast attention forward. q8 [B,H,N,d], k8/v8 [B,Hkv,N,d] E4M3 codes on the
+    same GPU; descales float32 [B,H] / [B,Hkv]. Returns float32 [B,H,N,d] (``out`` if given).
+    Enqueued on ``stream`` (default: the current stream); not synchronised."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    B, H, Hkv, N, d = _shapes(q8, k8, v8)
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    rc = lib.fp8_attn_fwd(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                          qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_fwd")
+    return out
+
+
+def p_collapse_count(q8, k8, q_descale, k_descale, *, causal: bool, kv_order: str = "reverse",
+                     S: float = 256.0, n_sink: int = 4, out=None, stream=None):
+    """Collapse counts (int64 [4] device tensor holding the library's uint64 counters):
+    [collapsed non-sink P, of which in sink blocks, non-sink pairs, of which in sink blocks]."""
+    import torch
+
+    lib = load()
+    q8, k8 = _as_codes(q8, "q"), _as_codes(k8, "k")
+    B, H, Hkv, N, d = _shapes(q8, k8)
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    if out is None:
+        out = torch.empty(4, dtype=torch.int64, device=dev)
+    rc = lib.fp8_attn_p_collapse_count(q8.data_ptr(), k8.data_ptr(), B, H, Hkv, N, d,
+                                       int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                                       qd.data_ptr(), kd.data_ptr(), int(n_sink), out.data_ptr(),
+                                       _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_p_collapse_count")
+    return out
+
+
+def kv_block() -> int:
+    return load().fp8_attn_kv_block()
+
+
+def version() -> str:
+    return load().fp8_attn_version().decode()

@@ -1,0 +1,110 @@
+// C ABI of the FP8 P-cast attention forward (declared in include/fp8attn.h).
+// Every argument is checked here before any HIP call; kernels live in fwd.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fp8attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Shared checks of the shapes, flags and scale. Returns FP8ATTN_OK or a negative status.
+int check_common(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FP8ATTN_EINVAL;
+  if (H % Hkv != 0) return FP8ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return FP8ATTN_EINVAL;
+  if (kv_order != FP8ATTN_KV_FORWARD && kv_order != FP8ATTN_KV_REVERSE) return FP8ATTN_EINVAL;
+  if (!(S > 0.0f && S <= kE4M3Max)) return FP8ATTN_EINVAL;   // also rejects NaN
+  if (d != 64 && d != 128 && d != 256) return FP8ATTN_EUNSUPPORTED;
+  if (N % fp8attn::kKvBlock != 0) return FP8ATTN_EUNSUPPORTED;
+  const int64_t tiles = (N + fp8attn::kBlockM - 1) / fp8attn::kBlockM;
+  if ((int64_t)B * H * tiles > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  return FP8ATTN_OK;
+}
+
+fp8attn::Params make_params(const void* q, const void* k, const void* v, float* o,
+                            int B, int H, int Hkv, int N, int d, int causal, int kv_order,
+                            float S, const float* qd, const float* kd, const float* vd,
+                            int n_sink, unsigned long long* counts) {
+  fp8attn::Params p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = o;
+  p.q_descale = qd;
+  p.k_descale = kd;
+  p.v_descale = vd;
+  p.counts = counts;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.N = N;
+  p.causal = causal;
+  p.reverse = kv_order == FP8ATTN_KV_REVERSE;
+  p.n_sink = n_sink;
+  p.S = S;
+  int e2 = 0;
+  const float mant = frexpf(S, &e2);
+  p.log2_S = (float)(e2 - 1);
+  (void)mant;
+  p.log2e_rsqrt_d = (float)(1.4426950408889634 / sqrt((double)d));
+  return p;
+}
+
+bool is_pow2(float S) {
+  int e2 = 0;
+  return frexpf(S, &e2) == 0.5f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_attn_fwd(const void* q, const void* k, const void* v, float* o,
+                 int B, int H, int Hkv, int N, int d,
+                 int causal, int kv_order, float S,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FP8ATTN_EUNSUPPORTED;
+  const fp8attn::Params p = make_params(q, k, v, o, B, H, Hkv, N, d, causal, kv_order, S,
+                                        q_descale, k_descale, v_descale, 0, nullptr);
+  const hipError_t e = fp8attn::launch_fwd(p, d, is_pow2(S), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
+int fp8_attn_p_collapse_count(const void* q, const void* k,
+                              int B, int H, int Hkv, int N, int d,
+                              int causal, int kv_order, float S,
+                              const float* q_descale, const float* k_descale,
+                              int n_sink, unsigned long long* counts, void* stream) {
+  if (!q || !k || !q_descale || !k_descale || !counts) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (n_sink < 0 || n_sink > N) return FP8ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k)) return FP8ATTN_EUNSUPPORTED;
+  const fp8attn::Params p = make_params(q, k, nullptr, nullptr, B, H, Hkv, N, d, causal, kv_order, S,
+                                        q_descale, k_descale, nullptr, n_sink, counts);
+  const hipError_t e = fp8attn::launch_count(p, d, is_pow2(S), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
+int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
+
+const char* fp8_attn_version(void) { return "fp8attn-gfx950 0.1.0"; }
+
+const char* fp8_attn_status_string(int status) {
+  switch (status) {
+    case FP8ATTN_OK: return "ok";
+    case FP8ATTN_EINVAL: return "invalid argument";
+    case FP8ATTN_EUNSUPPORTED: return "unsupported shape or alignment";
+    case FP8ATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// FP8 (OCP E4M3) P-cast attention forward for gfx950 (MI355X).
+//
+// Computation: "P-Cast Precision in FP8 Attention" (gist.science technical summary),
+// section 1: Q.K^T and P.V on E4M3 operands with an online softmax (running max m
+// updated per KV block), P~ multiplied by a static scale S and cast to E4M3 before the
+// P.V product, S divided back out in the epilogue, KV blocks walked forward or reverse.
+//
+// Layout of the work on the chip
+// ------------------------------
+// * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32
+//   rows. K/V blocks of 64 keys stream through LDS (two stages, double-buffered).
+// * Both GEMMs use v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32).
+// * Q.K^T is computed transposed, S^T = K . Q^T (A = 32 keys of K, B = 32 query rows of
+//   Q), so in the result each lane holds one query row: lane l has query col = l % 32
+//   and, for half = l / 32, the keys 8*(r/4) + 4*half + (r%4), r = 0..15, of each
+//   32-key tile. Row max and row sum are lane-local plus one exchange between the two
+//   lane halves; the running state (m, l) lives in the lane.
+// * P never leaves registers: the 32 fp32 probabilities of a lane are packed to E4M3
+//   four per dword (v_cvt_pk_fp8_f32), then the two lane halves trade one dword per
+//   pair so that every dword pair holds 8 consecutive keys; that pair layout is the B
+//   operand of O^T = V^T . P^T (32 output columns x 32 query rows per MFMA).
+// * V^T comes straight from the row-major V tile in LDS with ds_read_b64_tr_b8: within
+//   each 16-lane group, lane t receives byte t%8 of the 8-byte rows supplied by lanes
+//   2e + t/8 (e = 0..7); supplying 8 consecutive key rows x 16 columns gives each lane
+//   8 consecutive keys of one column, the same key order as the P pairs.
+// * LDS rows are XOR-swizzled at 16-byte granularity (chunk ^ (row % 8)) so that both
+//   the 128-bit K reads and the transposing V reads hit distinct banks.
+// * The MFMA operand k-slot order is only required to agree between A and B, so the d
+//   index of Q and K and the key index of P and V may be permuted consistently.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "launch.h"
+
+namespace fp8attn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // cbsz/blgp format 0 = E4M3 for both operands; zero scale operands select the
+  // unscaled instruction.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Map the linear workgroup id to (b, h, query tile). Workgroups are dispatched to the
+// 8 XCDs round-robin (id % 8); when the kv heads divide evenly, every XCD gets whole kv
+// heads (all their query heads), so K/V of one head stay in one XCD's L2, and within an
+// XCD the tiles run longest-first for causal masking.
+__device__ __forceinline__ void decode_tile(const Params& p, int ntiles, int& b, int& h, int& hk, int& qt) {
+  const int G = p.H / p.Hkv;
+  const int U = p.B * p.Hkv;
+  const int total = U * G * ntiles;
+  const int L = blockIdx.x;
+  int rank, unit, member;
+  if ((total & 7) == 0 && (U & 7) == 0) {
+    const int xcd = L & 7, slot = L >> 3;
+    const int upx = U >> 3;
+    const int per_rank = upx * G;
+    rank = slot / per_rank;
+    const int rem = slot - rank * per_rank;
+    unit = xcd * upx + rem / G;
+    member = rem % G;
+  } else {
+    const int BH = p.B * p.H;
+    rank = L / BH;
+    const int bh = L - rank * BH;
+    unit = bh / G;
+    member = bh % G;
+  }
+  b = unit / p.Hkv;
+  hk = unit - b * p.Hkv;
+  h = hk * G + member;
+  qt = p.causal ? (ntiles - 1 - rank) : rank;
+}
+
+template <int D, bool POW2, bool COUNT>
+__global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
+  constexpr int DM = D / 64;             // QK^T MFMAs per 32-key tile (k = 64 of d each)
+  constexpr int DU = D / 32;             // 32-column output tiles
+  constexpr int CH = D / 16;             // 16-byte chunks per row
+  constexpr int SWZ = (CH >= 8 ? 8 : CH) - 1;
+  constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
+  constexpr int STAGE = 2 * TILE;
+  constexpr int NTILES = COUNT ? 1 : 2;    // the count path never touches V
+  constexpr int NCH = NTILES * TILE / 16 / 256;   // 16-byte chunks each thread stages per block
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const int ntiles = (p.N + kBlockM - 1) / kBlockM;
+  int b, h, hk, qt;
+  decode_tile(p, ntiles, b, h, hk, qt);
+
+  const int i0 = qt * kBlockM;
+  const int r0 = i0 + wave * kRowsPerWave;
+  const bool wave_valid = r0 < p.N;
+  const int nkb = p.N / kKvBlock;
+  const int last_row = min(i0 + kBlockM, p.N) - 1;
+  const int wg_nb = p.causal ? (last_row / kKvBlock + 1) : nkb;
+  const int diag = r0 / kKvBlock;
+  const int wave_nb = p.causal ? (diag + 1) : nkb;
+
+  const size_t q_head = ((size_t)b * p.H + h) * (size_t)p.N * D;
+  const size_t kv_head = ((size_t)b * p.Hkv + hk) * (size_t)p.N * D;
+  const uint8_t* __restrict__ Kg = p.k + kv_head;
+  const uint8_t* __restrict__ Vg = p.v + kv_head;
+
+  // logits in log2 units: s' = raw . c with c = qd kd log2(e) / sqrt(d)
+  const float c = p.q_descale[b * p.H + h] * p.k_descale[b * p.Hkv + hk] * p.log2e_rsqrt_d;
+
+  // Q operand (B of S^T = K Q^T): lane (col, half) holds q[r0+col][64m + 32 half .. +32]
+  i32x8 qop[DM];
+  if (wave_valid) {
+    const uint8_t* qrow = p.q + q_head + (size_t)(r0 + col) * D + 32 * half;
+#pragma unroll
+    for (int m = 0; m < DM; ++m) {
+      const i32x4 lo = *(const i32x4*)(qrow + 64 * m);
+      const i32x4 hi = *(const i32x4*)(qrow + 64 * m + 16);
+      qop[m] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+
+  // ---- global -> register -> LDS staging of one K/V block
+  i32x4 stg[NCH];
+  auto gload = [&](int blk) {
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int qidx = tid + 256 * r;
+      const int tile = qidx / (TILE / 16);
+      const int qq = qidx - tile * (TILE / 16);
+      const int j = qq / CH, c16 = qq - (qq / CH) * CH;
+      const uint8_t* src = (tile ? Vg : Kg) + (size_t)(blk * kKvBlock + j) * D + c16 * 16;
+      stg[r] = *(const i32x4*)src;
+    }
+  };
+  auto swrite = [&](int stage) {
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int qidx = tid + 256 * r;
+      const int tile = qidx / (TILE / 16);
+      const int qq = qidx - tile * (TILE / 16);
+      const int j = qq / CH, c16 = qq - (qq / CH) * CH;
+      uint8_t* dst = smem + stage * STAGE + tile * TILE + j * D + ((c16 ^ (j & SWZ)) << 4);
+      *(i32x4*)dst = stg[r];
+    }
+  };
+
+  float m_run = -INFINITY;   // running max (log2 units)
+  float l_run = 0.f;         // this lane half's share of the row sum of P~ S
+  f32x16 acc[DU];
+#pragma unroll
+  for (int u = 0; u < DU; ++u) acc[u] = f32x16{0};
+  unsigned cnt_zero = 0, cnt_zero_sink = 0, cnt_pairs = 0, cnt_pairs_sink = 0;
+  const float bias_s = POW2 ? p.log2_S : 0.f;
+  const int i_row = r0 + col;
+
+  gload(p.reverse ? wg_nb - 1 : 0);
+  swrite(0);
+  __syncthreads();
+
+  for (int n = 0; n < wg_nb; ++n) {
+    const int blk = p.reverse ? (wg_nb - 1 - n) : n;
+    if (n + 1 < wg_nb) gload(p.reverse ? (wg_nb - 2 - n) : (n + 1));
+
+    if (wave_valid && blk < wave_nb) {
+      const uint8_t* Ks = smem + (n & 1) * STAGE;
+      const uint8_t* Vs = Ks + TILE;
+
+      // ---- S^T = K . Q^T for the two 32-key tiles of the block
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{0};
+        const int j = 32 * t + col;
+        const uint8_t* krow = Ks + j * D;
+#pragma unroll
+        for (int m = 0; m < DM; ++m) {
+          const int c16 = 4 * m + 2 * half;
+          const i32x4 lo = *(const i32x4*)(krow + ((c16 ^ (j & SWZ)) << 4));
+          const i32x4 hi = *(const i32x4*)(krow + (((c16 + 1) ^ (j & SWZ)) << 4));
+          s[t] = mfma_e4m3(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qop[m], s[t]);
+        }
+      }
+
+      // ---- causal mask on the wave's diagonal block (key j > query i)
+      if (p.causal && blk == diag) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = blk * kKvBlock + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (j > i_row) s[t][r] = -INFINITY;
+          }
+      }
+
+      // ---- running max: raw maximum, scaled once (c > 0 keeps the order)
+      float mx = s[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
+      m_run = m_new;
+      const float bias = bias_s - m_new;
+
+      // ---- P~ S (exp2 with log2 S folded in for S = 2^k), row sum, E4M3 cast
+      int pw[8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float x0 = fast_exp2(fmaf(s[t][4 * a + 0], c, bias));
+          float x1 = fast_exp2(fmaf(s[t][4 * a + 1], c, bias));
+          float x2 = fast_exp2(fmaf(s[t][4 * a + 2], c, bias));
+          float x3 = fast_exp2(fmaf(s[t][4 * a + 3], c, bias));
+          if (!POW2) { x0 *= p.S; x1 *= p.S; x2 *= p.S; x3 *= p.S; }
+          lsum += (x0 + x1) + (x2 + x3);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+          pw[4 * t + a] = w;
+        }
+      l_run = alpha * l_run + lsum;
+
+      if (COUNT) {
+        const bool sink_block = blk * kKvBlock < p.n_sink;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = blk * kKvBlock + 32 * t + 8 * a + 4 * half + e;
+              const bool live = (!p.causal || j <= i_row) && j >= p.n_sink;
+              const bool zero = ((pw[4 * t + a] >> (8 * e)) & 0xff) == 0;
+              cnt_pairs += live;
+              cnt_zero += live && zero;
+              if (sink_block) {
+                cnt_pairs_sink += live;
+                cnt_zero_sink += live && zero;
+              }
+            }
+      } else {
+#pragma unroll
+        for (int u = 0; u < DU; ++u) acc[u] *= alpha;
+
+        // ---- P pairs of 8 consecutive keys: lower half keeps X and takes the upper
+        // half's X; upper half takes the lower half's Y and keeps Y.
+        // v_permlane32_swap(X, Y) swaps X's upper 32 lanes with Y's lower 32 lanes.
+        i32x8 pop;
+#pragma unroll
+        for (int tw = 0; tw < 4; ++tw) {
+          const auto r = __builtin_amdgcn_permlane32_swap(pw[2 * tw], pw[2 * tw + 1], false, false);
+          pop[2 * tw] = (int)r[0];
+          pop[2 * tw + 1] = (int)r[1];
+        }
+
+        // ---- O^T += V^T . P^T, V^T read transposed from the row-major V tile
+        const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+          i32x8 vop;
+#pragma unroll
+          for (int tw = 0; tw < 4; ++tw) {
+            const int j = 32 * (tw >> 1) + 16 * (tw & 1) + 8 * (g >> 1) + (sl >> 1);
+            const int cc = 32 * u + 16 * (g & 1) + 8 * (sl & 1);
+            const int off = j * D + ((((cc >> 4) ^ (j & SWZ))) << 4) + (cc & 15);
+            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + off));
+            vop[2 * tw] = r.x;
+            vop[2 * tw + 1] = r.y;
+          }
+          acc[u] = mfma_e4m3(vop, pop, acc[u]);
+        }
+      }
+    }
+
+    if (n + 1 < wg_nb) swrite((n + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!wave_valid) return;
+  if (COUNT) {
+    unsigned v0 = cnt_zero, v1 = cnt_zero_sink, v2 = cnt_pairs, v3 = cnt_pairs_sink;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      v0 += __shfl_xor(v0, off);
+      v1 += __shfl_xor(v1, off);
+      v2 += __shfl_xor(v2, off);
+      v3 += __shfl_xor(v3, off);
+    }
+    if (lane == 0) {
+      atomicAdd(p.counts + 0, (unsigned long long)v0);
+      atomicAdd(p.counts + 1, (unsigned long long)v1);
+      atomicAdd(p.counts + 2, (unsigned long long)v2);
+      atomicAdd(p.counts + 3, (unsigned long long)v3);
+    }
+  } else {
+    // O = acc vd / (sum of P~ S) = acc vd / (S l); both halves hold partial row sums.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float scale = p.v_descale[b * p.Hkv + hk] / l_tot;
+    float* orow = p.o + q_head + (size_t)i_row * D + 4 * half;
+#pragma unroll
+    for (int u = 0; u < DU; ++u)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 val = {acc[u][4 * a + 0] * scale, acc[u][4 * a + 1] * scale,
+                           acc[u][4 * a + 2] * scale, acc[u][4 * a + 3] * scale};
+        *(f32x4*)(orow + 32 * u + 8 * a) = val;
+      }
+  }
+}
+
+__global__ void zero_counts_kernel(unsigned long long* counts) {
+  if (threadIdx.x < 4) counts[threadIdx.x] = 0ull;
+}
+
+template <bool COUNT>
+hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
+  const dim3 grid((unsigned)num_workgroups(p)), block(256);
+#define FP8ATTN_LAUNCH(D)                                                                    \
+  if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, COUNT>), grid, block, 0, stream, p);    \
+  else hipLaunchKernelGGL((fwd_kernel<D, false, COUNT>), grid, block, 0, stream, p);
+  switch (d) {
+    case 64: FP8ATTN_LAUNCH(64) break;
+    case 128: FP8ATTN_LAUNCH(128) break;
+    case 256: FP8ATTN_LAUNCH(256) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FP8ATTN_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
+  return launch<false>(p, d, pow2_scale, stream);
+}
+
+hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch<true>(p, d, pow2_scale, stream);
+}
+
+}  // namespace fp8attn

@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: the library loads, exports every function declared in
+include/*.h, and validates arguments before any HIP call (so these run on the CPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from precision_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # a 16-byte aligned non-null address; never dereferenced here
+
+
+def _declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(fp8_attn_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libfp8attn.so is not built; run __graft_entry__.build()")
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"fp8_attn_fwd", "fp8_attn_p_collapse_count"} <= set(names)
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_metadata(lib):
+    assert lib.fp8_attn_kv_block() == 64
+    assert lib.fp8_attn_version().decode().startswith("fp8attn")
+    assert lib.fp8_attn_status_string(0) == b"ok"
+    assert lib.fp8_attn_status_string(-2).startswith(b"unsupported")
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=1,
+         S=256.0, qd=FAKE, kd=FAKE, vd=FAKE):
+    return lib.fp8_attn_fwd(q, k, v, o, B, H, Hkv, N, d, causal, order, S, qd, kd, vd, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(qd=None), -1), (dict(kd=None), -1), (dict(vd=None), -1),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(d=0), -1),
+    (dict(H=3, Hkv=2), -1), (dict(causal=2), -1), (dict(order=2), -1), (dict(order=-1), -1),
+    (dict(S=0.0), -1), (dict(S=-1.0), -1), (dict(S=449.0), -1), (dict(S=512.0), -1),
+    (dict(S=float("nan")), -1), (dict(S=float("inf")), -1),
+    (dict(d=96), -2), (dict(d=32), -2), (dict(N=100), -2), (dict(N=96), -2),
+    (dict(q=FAKE + 8), -2), (dict(k=FAKE + 4), -2), (dict(v=FAKE + 1), -2), (dict(o=FAKE + 12), -2),
+    (dict(B=1 << 20, H=1 << 10, Hkv=1, N=1 << 14), -2),
+])
+def test_fwd_validation(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_sink=-1), -1), (dict(n_sink=129), -1), (dict(counts=None), -1), (dict(q=None), -1),
+    (dict(S=500.0), -1), (dict(d=48), -2), (dict(q=FAKE + 2), -2),
+])
+def test_count_validation(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=1, S=256.0,
+             qd=FAKE, kd=FAKE, n_sink=4, counts=FAKE)
+    a.update(kw)
+    rc = lib.fp8_attn_p_collapse_count(a["q"], a["k"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                       a["causal"], a["order"], a["S"], a["qd"], a["kd"],
+                                       a["n_sink"], a["counts"], None)
+    assert rc == status
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.uint8)
+    d = torch.ones(1, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.fwd(x, x, x, d, d, d, causal=False)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The HIP path and its binding never reference the CPU oracle."""
+    pkg = os.path.join(ROOT, "precision_attention_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if path.endswith((".py", ".hip", ".h", ".cpp")):
+            src = open(path).read()
+            assert not re.search(r"^\s*(from\s+oracle\b|import\s+oracle\b)|\boracle\.", src, re.M), path
