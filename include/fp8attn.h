@@ -84,6 +84,15 @@ int fp8_attn_p_collapse_count(const void* q, const void* k,
                               const float* q_descale, const float* k_descale,
                               int n_sink, unsigned long long* counts, void* stream);
 
+/* The forward pass and the collapse diagnostic in one pass over the data: writes o exactly
+ * as fp8_attn_fwd does and counts[0..3] exactly as fp8_attn_p_collapse_count does (same
+ * arguments, same meaning, same ownership and error rules). */
+int fp8_attn_fwd_counted(const void* q, const void* k, const void* v, float* o,
+                         int B, int H, int Hkv, int N, int d,
+                         int causal, int kv_order, float S,
+                         const float* q_descale, const float* k_descale, const float* v_descale,
+                         int n_sink, unsigned long long* counts, void* stream);
+
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);
 

@@ -25,6 +25,8 @@ def _declare(lib):
     lib.fp8_attn_fwd.restype = i
     lib.fp8_attn_p_collapse_count.argtypes = [vp, vp, i, i, i, i, i, i, i, f, vp, vp, i, vp, vp]
     lib.fp8_attn_p_collapse_count.restype = i
+    lib.fp8_attn_fwd_counted.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, vp, vp]
+    lib.fp8_attn_fwd_counted.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -137,6 +139,33 @@ def p_collapse_count(q8, k8, q_descale, k_descale, *, causal: bool, kv_order: st
                                        _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_p_collapse_count")
     return out
+
+
+def fwd_counted(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str = "reverse",
+                S: float = 256.0, n_sink: int = 4, out=None, counts=None, stream=None):
+    """Forward pass and collapse counts in one launch. Returns (O, counts) with the same
+    meaning as ``fwd`` and ``p_collapse_count``."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    B, H, Hkv, N, d = _shapes(q8, k8, v8)
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    if counts is None:
+        counts = torch.empty(4, dtype=torch.int64, device=dev)
+    rc = lib.fp8_attn_fwd_counted(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                  B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                                  qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink), counts.data_ptr(),
+                                  _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_fwd_counted")
+    return out, counts
 
 
 def kv_block() -> int:

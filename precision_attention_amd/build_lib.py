@@ -22,6 +22,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU forms anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every rounding exactly as written (explicit fmaf where a fused multiply-add is meant)
+    "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -93,6 +93,22 @@ int fp8_attn_p_collapse_count(const void* q, const void* k,
   return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
 }
 
+int fp8_attn_fwd_counted(const void* q, const void* k, const void* v, float* o,
+                         int B, int H, int Hkv, int N, int d,
+                         int causal, int kv_order, float S,
+                         const float* q_descale, const float* k_descale, const float* v_descale,
+                         int n_sink, unsigned long long* counts, void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale || !counts) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (n_sink < 0 || n_sink > N) return FP8ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FP8ATTN_EUNSUPPORTED;
+  const fp8attn::Params p = make_params(q, k, v, o, B, H, Hkv, N, d, causal, kv_order, S,
+                                        q_descale, k_descale, v_descale, n_sink, counts);
+  const hipError_t e = fp8attn::launch_fwd_count(p, d, is_pow2(S), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
 int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
 
 const char* fp8_attn_version(void) { return "fp8attn-gfx950 0.1.0"; }

@@ -82,7 +82,8 @@ __device__ __forceinline__ void decode_tile(const Params& p, int ntiles, int& b,
   qt = p.causal ? (ntiles - 1 - rank) : rank;
 }
 
-template <int D, bool POW2, bool COUNT>
+// OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
+template <int D, bool POW2, bool OUT, bool CNT>
 __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
   constexpr int DM = D / 64;             // QK^T MFMAs per 32-key tile (k = 64 of d each)
   constexpr int DU = D / 32;             // 32-column output tiles
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
   constexpr int SWZ = (CH >= 8 ? 8 : CH) - 1;
   constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
   constexpr int STAGE = 2 * TILE;
-  constexpr int NTILES = COUNT ? 1 : 2;    // the count path never touches V
+  constexpr int NTILES = OUT ? 2 : 1;      // a count-only launch never touches V
   constexpr int NCH = NTILES * TILE / 16 / 256;   // 16-byte chunks each thread stages per block
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
@@ -237,25 +238,39 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
         }
       l_run = alpha * l_run + lsum;
 
-      if (COUNT) {
+      if (CNT) {
         const bool sink_block = blk * kKvBlock < p.n_sink;
+        if ((p.causal && blk == diag) || sink_block) {
+          // blocks with masked or sink keys: test every element
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = blk * kKvBlock + 32 * t + 8 * a + 4 * half + e;
-              const bool live = (!p.causal || j <= i_row) && j >= p.n_sink;
-              const bool zero = ((pw[4 * t + a] >> (8 * e)) & 0xff) == 0;
-              cnt_pairs += live;
-              cnt_zero += live && zero;
-              if (sink_block) {
-                cnt_pairs_sink += live;
-                cnt_zero_sink += live && zero;
+              for (int e = 0; e < 4; ++e) {
+                const int j = blk * kKvBlock + 32 * t + 8 * a + 4 * half + e;
+                const bool live = (!p.causal || j <= i_row) && j >= p.n_sink;
+                const bool zero = ((pw[4 * t + a] >> (8 * e)) & 0xff) == 0;
+                cnt_pairs += live;
+                cnt_zero += live && zero;
+                if (sink_block) {
+                  cnt_pairs_sink += live;
+                  cnt_zero_sink += live && zero;
+                }
               }
-            }
-      } else {
+        } else {
+          // every key live and non-sink: count zero bytes of the packed codes. Codes are
+          // 0x00..0x7E, so byte + 0x7F never carries and has bit 7 set iff the code is
+          // nonzero.
+          unsigned nonzero = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            nonzero += __builtin_popcount(((unsigned)pw[q] + 0x7F7F7F7Fu) & 0x80808080u);
+          cnt_zero += 32u - nonzero;
+          cnt_pairs += 32u;
+        }
+      }
+      if (OUT) {
 #pragma unroll
         for (int u = 0; u < DU; ++u) acc[u] *= alpha;
 
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
   }
 
   if (!wave_valid) return;
-  if (COUNT) {
+  if (CNT) {
     unsigned v0 = cnt_zero, v1 = cnt_zero_sink, v2 = cnt_pairs, v3 = cnt_pairs_sink;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -309,7 +324,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
       atomicAdd(p.counts + 2, (unsigned long long)v2);
       atomicAdd(p.counts + 3, (unsigned long long)v3);
     }
-  } else {
+  }
+  if (OUT) {
     // O = acc vd / (sum of P~ S) = acc vd / (S l); both halves hold partial row sums.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float scale = p.v_descale[b * p.Hkv + hk] / l_tot;
@@ -329,12 +345,17 @@ __global__ void zero_counts_kernel(unsigned long long* counts) {
   if (threadIdx.x < 4) counts[threadIdx.x] = 0ull;
 }
 
-template <bool COUNT>
+template <bool OUT, bool CNT>
 hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
+  if (CNT) {
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)num_workgroups(p)), block(256);
-#define FP8ATTN_LAUNCH(D)                                                                    \
-  if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, COUNT>), grid, block, 0, stream, p);    \
-  else hipLaunchKernelGGL((fwd_kernel<D, false, COUNT>), grid, block, 0, stream, p);
+#define FP8ATTN_LAUNCH(D)                                                                       \
+  if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT>), grid, block, 0, stream, p);    \
+  else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT>), grid, block, 0, stream, p);
   switch (d) {
     case 64: FP8ATTN_LAUNCH(64) break;
     case 128: FP8ATTN_LAUNCH(128) break;
@@ -348,14 +369,15 @@ hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
-  return launch<false>(p, d, pow2_scale, stream);
+  return launch<true, false>(p, d, pow2_scale, stream);
 }
 
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch<true>(p, d, pow2_scale, stream);
+  return launch<false, true>(p, d, pow2_scale, stream);
+}
+
+hipError_t launch_fwd_count(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
+  return launch<true, true>(p, d, pow2_scale, stream);
 }
 
 }  // namespace fp8attn

@@ -9,12 +9,12 @@ namespace fp8attn {
 struct Params {
   const uint8_t* q;                 // [B][H][N][d] E4M3
   const uint8_t* k;                 // [B][Hkv][N][d] E4M3
-  const uint8_t* v;                 // [B][Hkv][N][d] E4M3 (unused by the count kernel)
-  float* o;                         // [B][H][N][d] fp32 (unused by the count kernel)
+  const uint8_t* v;                 // [B][Hkv][N][d] E4M3 (unused by a count-only launch)
+  float* o;                         // [B][H][N][d] fp32 (unused by a count-only launch)
   const float* q_descale;           // [B*H]
   const float* k_descale;           // [B*Hkv]
   const float* v_descale;           // [B*Hkv]
-  unsigned long long* counts;       // [4] (count kernel only)
+  unsigned long long* counts;       // [4] (launches that count)
   int B, H, Hkv, N;
   int causal, reverse, n_sink;
   float S;                          // static P scale
@@ -35,5 +35,6 @@ inline int64_t num_workgroups(const Params& p) {
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
+hipError_t launch_fwd_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 
 }  // namespace fp8attn

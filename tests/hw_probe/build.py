@@ -11,7 +11,7 @@ def build() -> str:
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     tmp = LIB + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off",
            "-I", HERE, os.path.join(HERE, "hw_probe.hip"), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -78,6 +78,20 @@ def test_count_validation(lib, kw, status):
     assert rc == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), -1), (dict(counts=None), -1), (dict(n_sink=-3), -1), (dict(S=0.0), -1),
+    (dict(H=5, Hkv=2), -1), (dict(d=80), -2), (dict(N=200), -2), (dict(v=FAKE + 4), -2),
+])
+def test_fwd_counted_validation(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=1, S=256.0,
+             qd=FAKE, kd=FAKE, vd=FAKE, n_sink=4, counts=FAKE)
+    a.update(kw)
+    rc = lib.fp8_attn_fwd_counted(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                  a["causal"], a["order"], a["S"], a["qd"], a["kd"], a["vd"], a["n_sink"],
+                                  a["counts"], None)
+    assert rc == status
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

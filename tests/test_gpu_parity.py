@@ -108,3 +108,23 @@ def test_float8_dtype_and_stream():
                         kv_order="reverse", S=256.0)
     s.synchronize()
     assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,order,S", [
+    (1, 4, 2, 1024, 128, True, "reverse", 256.0), (2, 2, 2, 640, 64, False, "forward", 1.0),
+    (1, 2, 1, 384, 256, True, "forward", 448.0)])
+def test_fused_equals_separate(B, H, Hkv, N, d, causal, order, S):
+    """fp8_attn_fwd_counted writes the same O (bitwise) as fp8_attn_fwd and the same
+    counts as fp8_attn_p_collapse_count."""
+    from precision_attention_amd import binding
+
+    inp = I.make_inputs(B, H, Hkv, N, d, delta=10.0, seed=7, descale="head", keep_float=False)
+    t = to_device(inp)
+    say(f"case fused B{B} H{H} N{N} d{d} causal={causal} {order} S={S}")
+    o = gpu_fwd(t, causal=causal, order=order, S=S)
+    c = gpu_counts(t, causal=causal, order=order, S=S)
+    of, cf = binding.fwd_counted(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], causal=causal,
+                                 kv_order=order, S=S, n_sink=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o, of)
+    assert np.array_equal(c, cf.cpu().numpy())
