@@ -24,6 +24,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # every rounding exactly as written (explicit fmaf where a fused multiply-add is meant)
     "-ffp-contract=off",
+    # keep MFMA sources/results in arch VGPRs: the softmax and the rescale are VALU work on
+    # them, and AGPR placement costs a v_accvgpr move per element and block
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -22,9 +22,30 @@ int check_common(int B, int H, int Hkv, int N, int d, int causal, int kv_order, 
   if (!(S > 0.0f && S <= kE4M3Max)) return FP8ATTN_EINVAL;   // also rejects NaN
   if (d != 64 && d != 128 && d != 256) return FP8ATTN_EUNSUPPORTED;
   if (N % fp8attn::kKvBlock != 0) return FP8ATTN_EUNSUPPORTED;
-  const int64_t tiles = (N + fp8attn::kBlockM - 1) / fp8attn::kBlockM;
+  const int bm = fp8attn::block_m_for(d);
+  const int64_t tiles = (N + bm - 1) / bm;
   if ((int64_t)B * H * tiles > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
   return FP8ATTN_OK;
+}
+
+// Unmasked non-sink (query, key) pairs over all B H heads, and those among them that lie in
+// KV blocks holding a sink token (keys n_sink .. E - 1, E = n_sink rounded up to a block).
+// Row i sees keys j <= i when causal, all N keys otherwise; keys j < n_sink are sinks.
+void pair_totals(int B, int H, int N, int causal, int n_sink, unsigned long long* all,
+                 unsigned long long* sink) {
+  const uint64_t n = (uint64_t)N, m = n - n_sink;
+  const uint64_t e = ((uint64_t)n_sink + fp8attn::kKvBlock - 1) / fp8attn::kKvBlock * fp8attn::kKvBlock;
+  const uint64_t k = e - n_sink;
+  uint64_t per_head_all, per_head_sink;
+  if (causal) {
+    per_head_all = m * (m + 1) / 2;                 // rows n_sink + x see x + 1 such keys
+    per_head_sink = k * (k + 1) / 2 + k * (n - e);  // rows below e, then k keys per row
+  } else {
+    per_head_all = n * m;
+    per_head_sink = n * k;
+  }
+  *all = (uint64_t)B * H * per_head_all;
+  *sink = (uint64_t)B * H * per_head_sink;
 }
 
 fp8attn::Params make_params(const void* q, const void* k, const void* v, float* o,
@@ -50,6 +71,7 @@ fp8attn::Params make_params(const void* q, const void* k, const void* v, float* 
   p.log2_S = (float)(e2 - 1);
   (void)mant;
   p.log2e_rsqrt_d = (float)(1.4426950408889634 / sqrt((double)d));
+  if (counts) pair_totals(B, H, N, causal, n_sink, &p.pairs, &p.pairs_sink);
   return p;
 }
 

@@ -42,6 +42,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, const f32x16& c) {
   // cbsz/blgp format 0 = E4M3 for both operands; zero scale operands select the
@@ -50,6 +51,14 @@ __device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, cons
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS row swizzle: 16-byte chunk c of row j lives at chunk c ^ swz(j). With
+// swz(j) = (j ^ j>>3) & 7 the 128-bit K-operand reads (16 consecutive rows, one chunk,
+// per cycle) hit distinct bank groups; the transposing V reads and the 128-bit staging
+// writes stay conflict-free as with a plain (j & 7) swizzle (measured with the LDS bank
+// conflict counters).
+template <int SWZ>
+__device__ __forceinline__ int swz_row(int j) { return (j ^ (j >> 3)) & SWZ; }
 
 // Map the linear workgroup id to (b, h, query tile). Workgroups are dispatched to the
 // 8 XCDs round-robin (id % 8); when the kv heads divide evenly, every XCD gets whole kv
@@ -82,18 +91,50 @@ __device__ __forceinline__ void decode_tile(const Params& p, int ntiles, int& b,
   qt = p.causal ? (ntiles - 1 - rank) : rank;
 }
 
+// Bit 7 of each of the first n bytes of a word (n clamped to 0 .. 4).
+__device__ __forceinline__ unsigned bytes_below(int n) {
+  return n >= 4 ? 0x80808080u : (n <= 0 ? 0u : (0x80808080u & ((1u << (8 * n)) - 1u)));
+}
+
+// One LDS-DMA instruction: every lane fetches 16 bytes at base + soff + voff (a raw buffer
+// of `range` bytes, so an offset past it reads zeros) and the wave's 64 x 16 bytes land
+// contiguously at lds_dst (lane L at byte 16 L). Completion is counted by vmcnt.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, int range, uint8_t* lds_dst,
+                                          int voff, int soff) {
+  constexpr int kRawBufferWord3 = 0x00020000;   // 32-bit data format, untyped access
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, kRawBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// The waves-per-SIMD floor is device code-generation information only. The host pass
+// leaves it out: given a template-dependent waves_per_eu it emits no launch stub.
+#ifdef __HIP_DEVICE_COMPILE__
+#define FP8ATTN_BOUNDS(threads, waves) __launch_bounds__(threads, waves)
+#else
+#define FP8ATTN_BOUNDS(threads, waves) __launch_bounds__(threads)
+#endif
+
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
 template <int D, bool POW2, bool OUT, bool CNT>
-__global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
+__global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_kernel(const Params p) {
+  constexpr int kWaves = waves_for(D);
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kBlockM = kRowsPerWave * kWaves;
   constexpr int DM = D / 64;             // QK^T MFMAs per 32-key tile (k = 64 of d each)
   constexpr int DU = D / 32;             // 32-column output tiles
   constexpr int CH = D / 16;             // 16-byte chunks per row
   constexpr int SWZ = (CH >= 8 ? 8 : CH) - 1;
+  auto swz = [](int j) { return swz_row<SWZ>(j); };
   constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
-  constexpr int STAGE = 2 * TILE;
-  constexpr int NTILES = OUT ? 2 : 1;      // a count-only launch never touches V
-  constexpr int NCH = NTILES * TILE / 16 / 256;   // 16-byte chunks each thread stages per block
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int STAGE = (OUT ? 2 : 1) * TILE;   // a count-only launch never touches V
+  // staging: one LDS-DMA instruction moves 64 lanes x 16 bytes = 1 KiB of a tile
+  constexpr int INST_PER_TILE = TILE / 1024;
+  constexpr int RPW = INST_PER_TILE / kWaves;    // per wave and tile
+  static_assert(INST_PER_TILE % kWaves == 0, "tile must split evenly over the waves");
+  // two separate stages, so the compiler can tell a DMA into one from reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,29 +175,55 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
     }
   }
 
-  // ---- global -> register -> LDS staging of one K/V block
-  i32x4 stg[NCH];
-  auto gload = [&](int blk) {
+  // ---- per-lane byte offsets, computed once: the loop adds only constants (stage base,
+  // row offsets), which the LDS instructions take as immediates.
+  // K operand of S^T = K.Q^T: key row 32t + col, 16-byte chunk (4m + 2 half + e) ^ swz(row).
+  // Row 32t + col swizzles like row col with bit 2 flipped, i.e. m ^ 1 when SWZ has bit 2.
+  constexpr int KT = (SWZ & 4) ? 1 : 0;
+  int koff[DM][2];
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int qidx = tid + 256 * r;
-      const int tile = qidx / (TILE / 16);
-      const int qq = qidx - tile * (TILE / 16);
-      const int j = qq / CH, c16 = qq - (qq / CH) * CH;
-      const uint8_t* src = (tile ? Vg : Kg) + (size_t)(blk * kKvBlock + j) * D + c16 * 16;
-      stg[r] = *(const i32x4*)src;
+  for (int m = 0; m < DM; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) koff[m][e] = col * D + (((4 * m + 2 * half + e) ^ swz(col)) << 4);
+  auto kaddr = [&](int t, int m, int e) { return koff[m ^ (KT * t)][e] + 32 * t * D; };
+  // V^T operand through the transpose read: within a 16-lane group g, lane sl supplies key
+  // row 16 tw + 8 (g >> 1) + (sl >> 1) and 8 columns of output tile u. Adding 16 tw to the
+  // row flips swizzle bits 2 tw, i.e. tile u reads like tile u ^ tw.
+  int voff[DU];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    const int j = 8 * (g >> 1) + (sl >> 1);
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int cc = 32 * u + 16 * (g & 1) + 8 * (sl & 1);
+      voff[u] = TILE + j * D + (((cc >> 4) ^ swz(j)) << 4) + (cc & 15);
+    }
+  }
+  auto vaddr = [&](int u, int tw) { return voff[u ^ (tw & (SWZ >> 1))] + 16 * tw * D; };
+  // LDS (row j, 16-byte slot cs) holds global chunk cs ^ swz(j) of row j. Instruction ii of
+  // a tile covers rows (1024 / D) ii .. and lane L lands on LDS bytes 16 L of that KiB, so
+  // it fetches the matching chunk. The offset within the tile is the same for K and V.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int goff[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int ii = wave + kWaves * r;
+    const int j = (1024 / D) * ii + lane / CH, cs = lane % CH;
+    goff[r] = j * D + ((cs ^ swz(j)) << 4);
+  }
+  auto dma = [&](int blk, uint8_t* stage) __attribute__((always_inline)) {
+    const int blk_off = blk * TILE;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      uint8_t* dst = stage + (wave_s + kWaves * r) * 1024;
+      lds_dma16(Kg, p.N * D, dst, goff[r], blk_off);
+      if (OUT) lds_dma16(Vg, p.N * D, dst + TILE, goff[r], blk_off);
     }
   };
-  auto swrite = [&](int stage) {
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int qidx = tid + 256 * r;
-      const int tile = qidx / (TILE / 16);
-      const int qq = qidx - tile * (TILE / 16);
-      const int j = qq / CH, c16 = qq - (qq / CH) * CH;
-      uint8_t* dst = smem + stage * STAGE + tile * TILE + j * D + ((c16 ^ (j & SWZ)) << 4);
-      *(i32x4*)dst = stg[r];
-    }
+  // every wave waits for its own DMA, then the barrier publishes all of them
+  auto dma_wait_sync = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
   };
 
   float m_run = -INFINITY;   // running max (log2 units)
@@ -164,34 +231,29 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
   f32x16 acc[DU];
 #pragma unroll
   for (int u = 0; u < DU; ++u) acc[u] = f32x16{0};
-  unsigned cnt_zero = 0, cnt_zero_sink = 0, cnt_pairs = 0, cnt_pairs_sink = 0;
+  unsigned cnt_zero = 0, cnt_zero_sink = 0;
   const float bias_s = POW2 ? p.log2_S : 0.f;
   const int i_row = r0 + col;
 
-  gload(p.reverse ? wg_nb - 1 : 0);
-  swrite(0);
-  __syncthreads();
+  dma(p.reverse ? wg_nb - 1 : 0, stage0);
+  dma_wait_sync();
 
-  for (int n = 0; n < wg_nb; ++n) {
+  // one block: compute on stage `cur` (a constant 0 or 1 at each call site), stage the
+  // next block into the other stage
+  auto step = [&](int n, int cur) __attribute__((always_inline)) {
     const int blk = p.reverse ? (wg_nb - 1 - n) : n;
-    if (n + 1 < wg_nb) gload(p.reverse ? (wg_nb - 2 - n) : (n + 1));
-
+    if (n + 1 < wg_nb) dma(p.reverse ? (wg_nb - 2 - n) : (n + 1), cur ? stage0 : stage1);
+    const uint8_t* Ks = cur ? stage1 : stage0;
     if (wave_valid && blk < wave_nb) {
-      const uint8_t* Ks = smem + (n & 1) * STAGE;
-      const uint8_t* Vs = Ks + TILE;
-
       // ---- S^T = K . Q^T for the two 32-key tiles of the block
       f32x16 s[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         s[t] = f32x16{0};
-        const int j = 32 * t + col;
-        const uint8_t* krow = Ks + j * D;
 #pragma unroll
         for (int m = 0; m < DM; ++m) {
-          const int c16 = 4 * m + 2 * half;
-          const i32x4 lo = *(const i32x4*)(krow + ((c16 ^ (j & SWZ)) << 4));
-          const i32x4 hi = *(const i32x4*)(krow + (((c16 + 1) ^ (j & SWZ)) << 4));
+          const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
+          const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
           s[t] = mfma_e4m3(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qop[m], s[t]);
         }
       }
@@ -213,7 +275,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      {
+        // the two lane halves trade maxima with v_permlane32_swap (no LDS round trip):
+        // the lower half finds the upper half's value in sw[1], the upper half in sw[0]
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
+      }
       const float m_new = fmaxf(m_run, mx * c);
       const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
       m_run = m_new;
@@ -239,40 +306,41 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
       l_run = alpha * l_run + lsum;
 
       if (CNT) {
-        const bool sink_block = blk * kKvBlock < p.n_sink;
+        // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
+        // carries and leaves bit 7 clear exactly for a zero code.
+        const int jb = blk * kKvBlock;
+        const bool sink_block = jb < p.n_sink;
         if ((p.causal && blk == diag) || sink_block) {
-          // blocks with masked or sink keys: test every element
+          // blocks with masked or sink keys: only keys j in [n_sink, hi] count, hi = i for
+          // causal attention. Word (t, a) holds keys base .. base + 3 in bytes 0 .. 3.
+          const int hi = p.causal ? i_row : p.N - 1;
+          unsigned z = 0;
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int j = blk * kKvBlock + 32 * t + 8 * a + 4 * half + e;
-                const bool live = (!p.causal || j <= i_row) && j >= p.n_sink;
-                const bool zero = ((pw[4 * t + a] >> (8 * e)) & 0xff) == 0;
-                cnt_pairs += live;
-                cnt_zero += live && zero;
-                if (sink_block) {
-                  cnt_pairs_sink += live;
-                  cnt_zero_sink += live && zero;
-                }
-              }
+            for (int a = 0; a < 4; ++a) {
+              const int base = jb + 32 * t + 8 * a + 4 * half;
+              const unsigned zero = ~((unsigned)pw[4 * t + a] + 0x7F7F7F7Fu) & 0x80808080u;
+              const unsigned live = bytes_below(hi - base + 1) & ~bytes_below(p.n_sink - base);
+              z += __builtin_popcount(zero & live);
+            }
+          cnt_zero += z;
+          if (sink_block) cnt_zero_sink += z;
         } else {
-          // every key live and non-sink: count zero bytes of the packed codes. Codes are
-          // 0x00..0x7E, so byte + 0x7F never carries and has bit 7 set iff the code is
-          // nonzero.
           unsigned nonzero = 0;
 #pragma unroll
           for (int q = 0; q < 8; ++q)
             nonzero += __builtin_popcount(((unsigned)pw[q] + 0x7F7F7F7Fu) & 0x80808080u);
           cnt_zero += 32u - nonzero;
-          cnt_pairs += 32u;
         }
       }
       if (OUT) {
+        // Rescale only when some row's max moved: alpha == 1 exactly otherwise, and a
+        // multiply by 1 changes nothing, so skipping it is exact.
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int u = 0; u < DU; ++u) acc[u] *= alpha;
+          for (int u = 0; u < DU; ++u) acc[u] *= alpha;
+        }
 
         // ---- P pairs of 8 consecutive keys: lower half keeps X and takes the upper
         // half's X; upper half takes the lower half's Y and keeps Y.
@@ -286,16 +354,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
         }
 
         // ---- O^T += V^T . P^T, V^T read transposed from the row-major V tile
-        const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
         for (int u = 0; u < DU; ++u) {
           i32x8 vop;
 #pragma unroll
           for (int tw = 0; tw < 4; ++tw) {
-            const int j = 32 * (tw >> 1) + 16 * (tw & 1) + 8 * (g >> 1) + (sl >> 1);
-            const int cc = 32 * u + 16 * (g & 1) + 8 * (sl & 1);
-            const int off = j * D + ((((cc >> 4) ^ (j & SWZ))) << 4) + (cc & 15);
-            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + off));
+            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Ks + vaddr(u, tw)));
             vop[2 * tw] = r.x;
             vop[2 * tw + 1] = r.y;
           }
@@ -303,28 +367,41 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
         }
       }
     }
-
-    if (n + 1 < wg_nb) swrite((n + 1) & 1);
-    __syncthreads();
+    dma_wait_sync();
+  };
+  for (int n = 0; n < wg_nb; n += 2) {
+    step(n, 0);
+    if (n + 1 < wg_nb) step(n + 1, 1);
   }
 
-  if (!wave_valid) return;
   if (CNT) {
-    unsigned v0 = cnt_zero, v1 = cnt_zero_sink, v2 = cnt_pairs, v3 = cnt_pairs_sink;
+    // Workgroup total of the zero counts (waves past the end of the sequence hold 0), then
+    // at most one atomic per counter and workgroup. The pair counters were set in closed
+    // form before the launch.
+    __shared__ unsigned red[2][kWaves];
+    unsigned v0 = cnt_zero, v1 = cnt_zero_sink;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       v0 += __shfl_xor(v0, off);
       v1 += __shfl_xor(v1, off);
-      v2 += __shfl_xor(v2, off);
-      v3 += __shfl_xor(v3, off);
     }
     if (lane == 0) {
-      atomicAdd(p.counts + 0, (unsigned long long)v0);
-      atomicAdd(p.counts + 1, (unsigned long long)v1);
-      atomicAdd(p.counts + 2, (unsigned long long)v2);
-      atomicAdd(p.counts + 3, (unsigned long long)v3);
+      red[0][wave] = v0;
+      red[1][wave] = v1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long z = 0, zs = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        z += red[0][w];
+        zs += red[1][w];
+      }
+      if (z) atomicAdd(p.counts + 0, z);
+      if (zs) atomicAdd(p.counts + 1, zs);
     }
   }
+  if (!wave_valid) return;
   if (OUT) {
     // O = acc vd / (sum of P~ S) = acc vd / (S l); both halves hold partial row sums.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -341,21 +418,30 @@ __global__ __launch_bounds__(256) void fwd_kernel(const Params p) {
   }
 }
 
-__global__ void zero_counts_kernel(unsigned long long* counts) {
-  if (threadIdx.x < 4) counts[threadIdx.x] = 0ull;
+// Zero counts start at 0; the pair counts are known in closed form before the launch.
+__global__ void init_counts_kernel(unsigned long long* counts, unsigned long long pairs,
+                                   unsigned long long pairs_sink) {
+  if (threadIdx.x == 0) {
+    counts[0] = 0ull;
+    counts[1] = 0ull;
+    counts[2] = pairs;
+    counts[3] = pairs_sink;
+  }
 }
 
 template <bool OUT, bool CNT>
 hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
   if (CNT) {
-    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts);
+    hipLaunchKernelGGL(init_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts, p.pairs, p.pairs_sink);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)num_workgroups(p)), block(256);
 #define FP8ATTN_LAUNCH(D)                                                                       \
-  if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT>), grid, block, 0, stream, p);    \
-  else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT>), grid, block, 0, stream, p);
+  {                                                                                             \
+    const dim3 grid((unsigned)num_workgroups(p, D)), block(64 * waves_for(D));                  \
+    if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT>), grid, block, 0, stream, p);  \
+    else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT>), grid, block, 0, stream, p);      \
+  }
   switch (d) {
     case 64: FP8ATTN_LAUNCH(64) break;
     case 128: FP8ATTN_LAUNCH(128) break;

@@ -15,6 +15,8 @@ struct Params {
   const float* k_descale;           // [B*Hkv]
   const float* v_descale;           // [B*Hkv]
   unsigned long long* counts;       // [4] (launches that count)
+  unsigned long long pairs;         // unmasked non-sink (query, key) pairs, all heads
+  unsigned long long pairs_sink;    // of which in KV blocks holding a sink token
   int B, H, Hkv, N;
   int causal, reverse, n_sink;
   float S;                          // static P scale
@@ -22,14 +24,20 @@ struct Params {
   float log2e_rsqrt_d;              // log2(e)/sqrt(d), rounded once to fp32
 };
 
-// Rows of queries per workgroup (4 waves x 32 rows).
+// Each wave owns 32 query rows; a workgroup has 4 waves (128 rows), one per SIMD, which
+// share every K/V block staged in LDS. Several workgroups share a CU (see the register
+// budget below), so one workgroup's barrier stall is covered by the others.
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = 4;
-constexpr int kBlockM = kRowsPerWave * kWaves;
 constexpr int kKvBlock = 64;
 
-inline int64_t num_workgroups(const Params& p) {
-  const int64_t tiles = (p.N + kBlockM - 1) / kBlockM;
+constexpr int waves_for(int) { return 4; }
+// Register budget: at most 512 / n VGPRs per lane lets n waves share a SIMD.
+constexpr int min_waves_per_simd(int d) { return d == 256 ? 2 : 3; }
+constexpr int block_m_for(int d) { return kRowsPerWave * waves_for(d); }
+
+inline int64_t num_workgroups(const Params& p, int d) {
+  const int bm = block_m_for(d);
+  const int64_t tiles = (p.N + bm - 1) / bm;
   return (int64_t)p.B * p.H * tiles;
 }
 
