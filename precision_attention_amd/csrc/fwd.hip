@@ -127,14 +127,18 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   constexpr int SWZ = (CH >= 8 ? 8 : CH) - 1;
   auto swz = [](int j) { return swz_row<SWZ>(j); };
   constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
-  constexpr int STAGE = (OUT ? 2 : 1) * TILE;   // a count-only launch never touches V
   // staging: one LDS-DMA instruction moves 64 lanes x 16 bytes = 1 KiB of a tile
   constexpr int INST_PER_TILE = TILE / 1024;
   constexpr int RPW = INST_PER_TILE / kWaves;    // per wave and tile
   static_assert(INST_PER_TILE % kWaves == 0, "tile must split evenly over the waves");
-  // two separate stages, so the compiler can tell a DMA into one from reads of the other
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+  // Double buffers for K and V, four separate arrays so that the compiler can tell a DMA
+  // into one buffer from reads of another: K(n), V(n) are read while block n + 1 lands.
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[OUT ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[OUT ? TILE : 16];
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? kb1 : kb0; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return i ? vb1 : vb0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -175,7 +179,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     }
   }
 
-  // ---- per-lane byte offsets, computed once: the loop adds only constants (stage base,
+  // ---- per-lane byte offsets, computed once: the loop adds only constants (buffer base,
   // row offsets), which the LDS instructions take as immediates.
   // K operand of S^T = K.Q^T: key row 32t + col, 16-byte chunk (4m + 2 half + e) ^ swz(row).
   // Row 32t + col swizzles like row col with bit 2 flipped, i.e. m ^ 1 when SWZ has bit 2.
@@ -196,7 +200,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int cc = 32 * u + 16 * (g & 1) + 8 * (sl & 1);
-      voff[u] = TILE + j * D + (((cc >> 4) ^ swz(j)) << 4) + (cc & 15);
+      voff[u] = j * D + (((cc >> 4) ^ swz(j)) << 4) + (cc & 15);
     }
   }
   auto vaddr = [&](int u, int tw) { return voff[u ^ (tw & (SWZ >> 1))] + 16 * tw * D; };
@@ -211,22 +215,23 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     const int j = (1024 / D) * ii + lane / CH, cs = lane % CH;
     goff[r] = j * D + ((cs ^ swz(j)) << 4);
   }
-  auto dma = [&](int blk, uint8_t* stage) __attribute__((always_inline)) {
-    const int blk_off = blk * TILE;
+  auto dma_tile = [&](const uint8_t* src, int blk, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      uint8_t* dst = stage + (wave_s + kWaves * r) * 1024;
-      lds_dma16(Kg, p.N * D, dst, goff[r], blk_off);
-      if (OUT) lds_dma16(Vg, p.N * D, dst + TILE, goff[r], blk_off);
-    }
+    for (int r = 0; r < RPW; ++r)
+      lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, goff[r], blk * TILE);
   };
   // every wave waits for its own DMA, then the barrier publishes all of them
   auto dma_wait_sync = []() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
   };
+  auto block_of = [&](int n) { return p.reverse ? (wg_nb - 1 - n) : n; };
+  auto active = [&](int n) { return wave_valid && block_of(n) < wave_nb; };
 
-  float m_run = -INFINITY;   // running max (log2 units)
+  // Running max (log2 units). It starts finite and far below any logit, so that a fully
+  // masked block (max -inf) leaves it and the row unchanged; the first real block still
+  // gets alpha = exp2(-1e30 - m) = 0.
+  float m_run = -1e30f;
   float l_run = 0.f;         // this lane half's share of the row sum of P~ S
   f32x16 acc[DU];
 #pragma unroll
@@ -235,147 +240,209 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   const float bias_s = POW2 ? p.log2_S : 0.f;
   const int i_row = r0 + col;
 
-  dma(p.reverse ? wg_nb - 1 : 0, stage0);
-  dma_wait_sync();
-
-  // one block: compute on stage `cur` (a constant 0 or 1 at each call site), stage the
-  // next block into the other stage
-  auto step = [&](int n, int cur) __attribute__((always_inline)) {
-    const int blk = p.reverse ? (wg_nb - 1 - n) : n;
-    if (n + 1 < wg_nb) dma(p.reverse ? (wg_nb - 2 - n) : (n + 1), cur ? stage0 : stage1);
-    const uint8_t* Ks = cur ? stage1 : stage0;
-    if (wave_valid && blk < wave_nb) {
-      // ---- S^T = K . Q^T for the two 32-key tiles of the block
-      f32x16 s[2];
+  // ---- S^T = K . Q^T for the two 32-key tiles of the block in Ks. For d <= 128 all
+  // operand reads are issued first (the registers are free at this point), so that one
+  // LDS latency covers them all; d = 256 has no room for that and pairs each MFMA with
+  // its two reads.
+  auto qk = [&](const uint8_t* Ks, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    auto kop = [&](int t, int m) __attribute__((always_inline)) {
+      const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
+      const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
+      return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    if (DM <= 2) {
+      i32x8 ko[2][DM];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < DM; ++m) ko[t][m] = kop(t, m);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         s[t] = f32x16{0};
 #pragma unroll
-        for (int m = 0; m < DM; ++m) {
-          const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
-          const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
-          s[t] = mfma_e4m3(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qop[m], s[t]);
-        }
+        for (int m = 0; m < DM; ++m) s[t] = mfma_e4m3(ko[t][m], qop[m], s[t]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * DM, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DM, 0);   // MFMA
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{0};
+#pragma unroll
+        for (int m = 0; m < DM; ++m) s[t] = mfma_e4m3(kop(t, m), qop[m], s[t]);
+      }
+    }
+  };
 
-      // ---- causal mask on the wave's diagonal block (key j > query i)
-      if (p.causal && blk == diag) {
+  // ---- V^T operand u of O^T += V^T . P^T, read transposed from the row-major V tile
+  auto read_v = [&](const uint8_t* Vs, int u) __attribute__((always_inline)) {
+    i32x8 vop;
+#pragma unroll
+    for (int tw = 0; tw < 4; ++tw) {
+      const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + vaddr(u, tw)));
+      vop[2 * tw] = r.x;
+      vop[2 * tw + 1] = r.y;
+    }
+    return vop;
+  };
+  // the first NVPRE V operands are read before the softmax, so that their LDS latency is
+  // spent under it
+  constexpr int NVPRE = D == 256 ? 0 : 1;   // d = 256 has no registers to spare
+  constexpr int NVARR = NVPRE > 0 ? NVPRE : 1;
+
+  // ---- online softmax of block blk with scores s: running max and sum, the rescale of O,
+  // the E4M3 cast of P (into pop, the B-operand layout of the P.V product) and the counts
+  auto softmax = [&](f32x16 (&s)[2], int blk, i32x8& pop) __attribute__((always_inline)) {
+    // causal mask (key j > query i) on the wave's diagonal block (blocks past it are
+    // never visited; the test covers them too)
+    if (p.causal && blk >= diag) {
+      // element (t, r) holds key blk * 64 + 4 half + k with k = 32t + 8(r / 4) + r % 4
+      const int rel = i_row - blk * kKvBlock - 4 * half;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + (r & 3) > rel) s[t][r] = -INFINITY;
+    }
+
+    // running max: raw maximum, scaled once (c > 0 keeps the order)
+    float mx = s[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    {
+      // the two lane halves trade maxima with v_permlane32_swap (no LDS round trip):
+      // the lower half finds the upper half's value in sw[1], the upper half in sw[0]
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
+    }
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
+    m_run = m_new;
+    const float bias = bias_s - m_new;
+
+    // P~ S (exp2 with log2 S folded in for S = 2^k), row sum, E4M3 cast. The first cast
+    // of a dword writes its low half and keeps the rest, which the second cast replaces,
+    // so the kept value is arbitrary (no register clearing).
+    int pw[8];   // E4M3 codes of P, four per dword
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float x0 = fast_exp2(fmaf(s[t][4 * a + 0], c, bias));
+        float x1 = fast_exp2(fmaf(s[t][4 * a + 1], c, bias));
+        float x2 = fast_exp2(fmaf(s[t][4 * a + 2], c, bias));
+        float x3 = fast_exp2(fmaf(s[t][4 * a + 3], c, bias));
+        if (!POW2) { x0 *= p.S; x1 *= p.S; x2 *= p.S; x3 *= p.S; }
+        lsum += (x0 + x1) + (x2 + x3);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_nondeterministic_value(0), false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+        pw[4 * t + a] = w;
+      }
+    l_run = alpha * l_run + lsum;
+
+    if (CNT) {
+      // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
+      // carries and leaves bit 7 clear exactly for a zero code.
+      const int jb = blk * kKvBlock;
+      const bool sink_block = jb < p.n_sink;
+      if ((p.causal && blk >= diag) || sink_block) {
+        // blocks with masked or sink keys: only keys j in [n_sink, hi] count, hi = i for
+        // causal attention.
+        const int hi = p.causal ? i_row : p.N - 1;
+        const int n_hi = hi - jb - 4 * half + 1, n_lo = p.n_sink - jb - 4 * half;
+        unsigned z = 0;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = blk * kKvBlock + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (j > i_row) s[t][r] = -INFINITY;
+          for (int a = 0; a < 4; ++a) {
+            const int k = 32 * t + 8 * a;   // word (t, a) holds keys jb + 4 half + k .. + 3
+            const unsigned zero = ~((unsigned)pw[4 * t + a] + 0x7F7F7F7Fu) & 0x80808080u;
+            const unsigned live = bytes_below(n_hi - k) & ~bytes_below(n_lo - k);
+            z += __builtin_popcount(zero & live);
           }
-      }
-
-      // ---- running max: raw maximum, scaled once (c > 0 keeps the order)
-      float mx = s[0][0];
+        cnt_zero += z;
+        if (sink_block) cnt_zero_sink += z;
+      } else {
+        unsigned nonzero = 0;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      {
-        // the two lane halves trade maxima with v_permlane32_swap (no LDS round trip):
-        // the lower half finds the upper half's value in sw[1], the upper half in sw[0]
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
-      }
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
-      m_run = m_new;
-      const float bias = bias_s - m_new;
-
-      // ---- P~ S (exp2 with log2 S folded in for S = 2^k), row sum, E4M3 cast
-      int pw[8];
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float x0 = fast_exp2(fmaf(s[t][4 * a + 0], c, bias));
-          float x1 = fast_exp2(fmaf(s[t][4 * a + 1], c, bias));
-          float x2 = fast_exp2(fmaf(s[t][4 * a + 2], c, bias));
-          float x3 = fast_exp2(fmaf(s[t][4 * a + 3], c, bias));
-          if (!POW2) { x0 *= p.S; x1 *= p.S; x2 *= p.S; x3 *= p.S; }
-          lsum += (x0 + x1) + (x2 + x3);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-          pw[4 * t + a] = w;
-        }
-      l_run = alpha * l_run + lsum;
-
-      if (CNT) {
-        // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
-        // carries and leaves bit 7 clear exactly for a zero code.
-        const int jb = blk * kKvBlock;
-        const bool sink_block = jb < p.n_sink;
-        if ((p.causal && blk == diag) || sink_block) {
-          // blocks with masked or sink keys: only keys j in [n_sink, hi] count, hi = i for
-          // causal attention. Word (t, a) holds keys base .. base + 3 in bytes 0 .. 3.
-          const int hi = p.causal ? i_row : p.N - 1;
-          unsigned z = 0;
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const int base = jb + 32 * t + 8 * a + 4 * half;
-              const unsigned zero = ~((unsigned)pw[4 * t + a] + 0x7F7F7F7Fu) & 0x80808080u;
-              const unsigned live = bytes_below(hi - base + 1) & ~bytes_below(p.n_sink - base);
-              z += __builtin_popcount(zero & live);
-            }
-          cnt_zero += z;
-          if (sink_block) cnt_zero_sink += z;
-        } else {
-          unsigned nonzero = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            nonzero += __builtin_popcount(((unsigned)pw[q] + 0x7F7F7F7Fu) & 0x80808080u);
-          cnt_zero += 32u - nonzero;
-        }
-      }
-      if (OUT) {
-        // Rescale only when some row's max moved: alpha == 1 exactly otherwise, and a
-        // multiply by 1 changes nothing, so skipping it is exact.
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int u = 0; u < DU; ++u) acc[u] *= alpha;
-        }
-
-        // ---- P pairs of 8 consecutive keys: lower half keeps X and takes the upper
-        // half's X; upper half takes the lower half's Y and keeps Y.
-        // v_permlane32_swap(X, Y) swaps X's upper 32 lanes with Y's lower 32 lanes.
-        i32x8 pop;
-#pragma unroll
-        for (int tw = 0; tw < 4; ++tw) {
-          const auto r = __builtin_amdgcn_permlane32_swap(pw[2 * tw], pw[2 * tw + 1], false, false);
-          pop[2 * tw] = (int)r[0];
-          pop[2 * tw + 1] = (int)r[1];
-        }
-
-        // ---- O^T += V^T . P^T, V^T read transposed from the row-major V tile
-#pragma unroll
-        for (int u = 0; u < DU; ++u) {
-          i32x8 vop;
-#pragma unroll
-          for (int tw = 0; tw < 4; ++tw) {
-            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Ks + vaddr(u, tw)));
-            vop[2 * tw] = r.x;
-            vop[2 * tw + 1] = r.y;
-          }
-          acc[u] = mfma_e4m3(vop, pop, acc[u]);
-        }
+        for (int q = 0; q < 8; ++q)
+          nonzero += __builtin_popcount(((unsigned)pw[q] + 0x7F7F7F7Fu) & 0x80808080u);
+        cnt_zero += 32u - nonzero;
       }
     }
-    dma_wait_sync();
+    if (OUT) {
+      // Rescale only when some row's max moved: alpha == 1 exactly otherwise, and a
+      // multiply by 1 changes nothing, so skipping it is exact.
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int u = 0; u < DU; ++u) acc[u] *= alpha;
+      }
+
+      // P pairs of 8 consecutive keys: lower half keeps X and takes the upper half's X;
+      // upper half takes the lower half's Y and keeps Y.
+      // v_permlane32_swap(X, Y) swaps X's upper 32 lanes with Y's lower 32 lanes.
+#pragma unroll
+      for (int tw = 0; tw < 4; ++tw) {
+        const auto r = __builtin_amdgcn_permlane32_swap(pw[2 * tw], pw[2 * tw + 1], false, false);
+        pop[2 * tw] = (int)r[0];
+        pop[2 * tw + 1] = (int)r[1];
+      }
+    }
   };
-  for (int n = 0; n < wg_nb; n += 2) {
-    step(n, 0);
-    if (n + 1 < wg_nb) step(n + 1, 1);
+
+  // ---- O^T += V^T . P^T with the V tile in Vs (operands u < NVPRE already read)
+  auto pv = [&](const uint8_t* Vs, const i32x8& pop, const i32x8 (&vpre)[NVARR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const i32x8 vop = u < NVPRE ? vpre[u < NVPRE ? u : 0] : read_v(Vs, u);
+      acc[u] = mfma_e4m3(vop, pop, acc[u]);
+    }
+    // issue order: each remaining MFMA right after its four operand reads
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      if (u >= NVPRE) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    }
+  };
+
+  i32x8 pop;   // P of the block, in the B-operand layout of the P.V product
+  {
+    dma_tile(Kg, block_of(0), kb0);
+    if (OUT) dma_tile(Vg, block_of(0), vb0);
+    dma_wait_sync();
+    // step n on buffers `cur` (a constant 0 or 1 at each call site); block n + 1 lands in
+    // the other pair
+    auto step = [&](int n, int cur) __attribute__((always_inline)) {
+      if (n + 1 < wg_nb) {
+        dma_tile(Kg, block_of(n + 1), kbuf(cur ^ 1));
+        if (OUT) dma_tile(Vg, block_of(n + 1), vbuf(cur ^ 1));
+      }
+      if (active(n)) {
+        f32x16 s[2];
+        qk(kbuf(cur), s);
+        i32x8 vpre[NVARR];
+        if (OUT) {
+#pragma unroll
+          for (int u = 0; u < NVPRE; ++u) vpre[u] = read_v(vbuf(cur), u);
+        }
+        softmax(s, block_of(n), pop);
+        if (OUT) pv(vbuf(cur), pop, vpre);
+      }
+      dma_wait_sync();
+    };
+    for (int n = 0; n < wg_nb; n += 2) {
+      step(n, 0);
+      if (n + 1 < wg_nb) step(n + 1, 1);
+    }
   }
 
   if (CNT) {
-    // Workgroup total of the zero counts (waves past the end of the sequence hold 0), then
+    // Waves past the end of the sequence (they ran on rows that do not exist) count nothing.
+    if (!wave_valid) cnt_zero = cnt_zero_sink = 0;
+    // Workgroup total of the zero counts, then
     // at most one atomic per counter and workgroup. The pair counters were set in closed
     // form before the launch.
     __shared__ unsigned red[2][kWaves];
