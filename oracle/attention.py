@@ -30,6 +30,16 @@ Readings taken where the pages leave a step open (each is listed in the design n
   * causal masking is j <= i with equal query and key lengths; a block that is
     entirely masked for a row leaves that row's state unchanged.
 
+Two variants beyond the pages' own two choices (order, S), each an option here:
+  * "reverse_sink_last": the reverse walk with block 0 split in two visits, its non-sink
+    keys [n_sink, 64) first and the sink keys [0, n_sink) last. It applies the pages'
+    reason for the reverse order (§2, Optimization 1: the sink should raise m only after
+    every other P has been cast) to the tokens that share block 0 with the sinks.
+  * denominator "quantized": l accumulates the decoded cast operand dec(P8) instead of
+    P~·S, so that the same quantized P feeds the numerator and the denominator (the
+    consistency idea of the EFQ-Softmax abstract, applied to the E4M3 cast); then
+    O = acc / l.
+
 Everything is fp64. Q·K^T is taken over the raw decoded E4M3 values, which is exact
 in fp64 (every product is a multiple of 2^-18 and every partial sum stays far below
 2^53 of those units), and the descales are applied afterwards.
@@ -88,9 +98,22 @@ def block_visit_order(n_keys: int, kv_order: str, block: int = BLOCK):
     nb = n_keys // block
     if kv_order == "forward":
         return list(range(nb))
-    if kv_order == "reverse":
+    if kv_order in ("reverse", "reverse_sink_last"):
         return list(range(nb - 1, -1, -1))
     raise ValueError(kv_order)
+
+
+def visit_units(n_keys: int, kv_order: str, block: int = BLOCK, n_sink: int = N_SINK_DEFAULT):
+    """The key ranges [start, end) in visit order; each range is one online-softmax step
+    (one running-max update). For "forward" and "reverse" they are the blocks. For
+    "reverse_sink_last" block 0 is visited as [n_sink, 64) and then [0, n_sink) (empty
+    ranges dropped; needs 0 <= n_sink <= block)."""
+    units = [(b * block, (b + 1) * block) for b in block_visit_order(n_keys, kv_order, block)]
+    if kv_order == "reverse_sink_last" and units:
+        if not 0 <= n_sink <= block:
+            raise ValueError("reverse_sink_last needs 0 <= n_sink <= block")
+        units = units[:-1] + [u for u in ((n_sink, block), (0, n_sink)) if u[1] > u[0]]
+    return units
 
 
 # --------------------------------------------------------------------------------------
@@ -108,25 +131,30 @@ def _cast(p_scaled, p_cast: str):
 
 
 def online_softmax_pcast(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
-                         block: int = BLOCK, keep_trace: bool = False):
+                         block: int = BLOCK, keep_trace: bool = False, n_sink: int = N_SINK_DEFAULT,
+                         denominator: str = "fp32"):
     """Run the block-wise online softmax with the P-cast for a set of rows.
 
     ``s``: [R, N] fp64 logits (-inf where masked). ``v``: [N, d] fp64 values (already
-    multiplied by their descale). For each row, blocks are visited in ``kv_order``;
-    per block:
+    multiplied by their descale). For each row, the key ranges of ``visit_units`` are
+    visited in order (the blocks, for forward and reverse); per range:
         m_new = max(m, max_j s_ij)
         alpha = exp(m - m_new)                     (0 while m = -inf)
         P~_ij = exp(s_ij - m_new)
         P8_ij = cast(P~_ij · S)
-        l     = alpha·l + sum_j P~_ij              (unquantized P~)
+        l     = alpha·l + sum_j P~_ij·S            (denominator "fp32": unquantized P~)
+          or  = alpha·l + sum_j P8_ij              (denominator "quantized")
         acc   = alpha·acc + sum_j P8_ij · v_j
         m     = m_new
-    and O = acc / (S·l). Rows are processed together but every row follows exactly
-    its own sequence; a block with no unmasked key for a row changes nothing for it.
+    and O = acc / l. (With "fp32", l carries the factor S, i.e. O = acc / (S · sum P~).)
+    Rows are processed together but every row follows exactly its own sequence; a range
+    with no unmasked key for a row changes nothing for it.
 
-    Returns (O [R, d], trace) where ``trace`` (if requested) holds, per visited block,
-    the block index, m after the block, P~ and the cast operand P8.
+    Returns (O [R, d], trace) where ``trace`` (if requested) holds, per visited range,
+    its bounds, m after it, P~ and the cast operand P8.
     """
+    if denominator not in ("fp32", "quantized"):
+        raise ValueError(denominator)
     s = np.asarray(s, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     R, N = s.shape
@@ -134,8 +162,8 @@ def online_softmax_pcast(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
     l = np.zeros(R)
     acc = np.zeros((R, v.shape[1]))
     trace = []
-    for b in block_visit_order(N, kv_order, block):
-        sb = s[:, b * block:(b + 1) * block]
+    for (j0, j1) in visit_units(N, kv_order, block, n_sink):
+        sb = s[:, j0:j1]
         live = np.isfinite(sb)                               # unmasked entries
         row_live = live.any(axis=1)
         bmax = np.where(live, sb, -np.inf).max(axis=1)
@@ -144,47 +172,57 @@ def online_softmax_pcast(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
             alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
             p = np.where(live, np.exp(sb - m_new[:, None]), 0.0)
         p8 = _cast(p * S, p_cast)
-        l = alpha * l + p.sum(axis=1)
-        acc = alpha[:, None] * acc + p8 @ v[b * block:(b + 1) * block]
+        l = alpha * l + (p.sum(axis=1) * S if denominator == "fp32" else p8.sum(axis=1))
+        acc = alpha[:, None] * acc + p8 @ v[j0:j1]
         m = m_new
         if keep_trace:
-            trace.append({"block": b, "m": m.copy(), "p": p, "p8": p8, "live": live})
-    o = acc / (S * l[:, None])
+            trace.append({"block": j0 // block, "range": (j0, j1), "m": m.copy(), "p": p, "p8": p8,
+                          "live": live})
+    o = acc / l[:, None]
     return o, trace
 
 
+def _running_max_at_key(s, kv_order, block, n_sink=N_SINK_DEFAULT):
+    """m_u(i) at every key: row i's running max right after visiting the range that holds
+    key j, and the final max m_f(i)."""
+    R, N = s.shape
+    fin = np.where(np.isfinite(s), s, -np.inf)
+    m_at_key = np.full((R, N), -np.inf)
+    cur = np.full(R, -np.inf)
+    for (j0, j1) in visit_units(N, kv_order, block, n_sink):
+        cur = np.maximum(cur, fin[:, j0:j1].max(axis=1))
+        m_at_key[:, j0:j1] = cur[:, None]
+    return m_at_key, cur
+
+
 def online_softmax_pcast_vectorized(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3",
-                                    block: int = BLOCK):
+                                    block: int = BLOCK, n_sink: int = N_SINK_DEFAULT,
+                                    denominator: str = "fp32"):
     """The same result written in closed form instead of as a recurrence.
 
-    Let m_b(i) be row i's running max right after visiting block b and m_f(i) the final
-    max. Unrolling the recurrence, block b's contribution is rescaled by every later
-    alpha, i.e. by exp(m_b - m_f), and the row sum telescopes to sum_j exp(s_ij - m_f):
+    Let m_u(i) be row i's running max right after visiting range u and m_f(i) the final
+    max. Unrolling the recurrence, range u's contribution is rescaled by every later
+    alpha, i.e. by exp(m_u - m_f), and the row sum telescopes:
 
-        O_i = sum_j cast(exp(s_ij - m_b(j)(i))·S)·exp(m_b(j)(i) - m_f(i))·v_j
-              / (S · sum_j exp(s_ij - m_f(i)))
+        O_i = sum_j cast(exp(s_ij - m_u(j)(i))·S)·exp(m_u(j)(i) - m_f(i))·v_j / L_i
+        L_i = S · sum_j exp(s_ij - m_f(i))                                ("fp32")
+            = sum_j cast(exp(s_ij - m_u(j)(i))·S)·exp(m_u(j)(i) - m_f(i))  ("quantized")
 
-    where b(j) is the block of key j. Equal to the recurrence in real arithmetic.
+    where u(j) is the range holding key j. Equal to the recurrence in real arithmetic.
     """
     s = np.asarray(s, dtype=np.float64)
-    R, N = s.shape
-    order = block_visit_order(N, kv_order, block)
-    nb = N // block
-    bmax = np.where(np.isfinite(s), s, -np.inf).reshape(R, nb, block).max(axis=2)   # [R, nb]
-    run = np.full((R, nb), -np.inf)
-    cur = np.full(R, -np.inf)
-    for b in order:
-        cur = np.maximum(cur, bmax[:, b])
-        run[:, b] = cur
-    m_f = cur
-    m_at_key = np.repeat(run, block, axis=1)                                       # [R, N]
+    m_at_key, m_f = _running_max_at_key(s, kv_order, block, n_sink)
     live = np.isfinite(s)
     with np.errstate(invalid="ignore"):
         p = np.where(live, np.exp(s - m_at_key), 0.0)
         w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
-        l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1)
+        l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1) * S
     p8 = _cast(p * S, p_cast)
-    return ((p8 * w) @ np.asarray(v, dtype=np.float64)) / (S * l[:, None])
+    if denominator == "quantized":
+        l = (p8 * w).sum(axis=1)
+    elif denominator != "fp32":
+        raise ValueError(denominator)
+    return ((p8 * w) @ np.asarray(v, dtype=np.float64)) / l[:, None]
 
 
 def exact_attention(s, v):
@@ -211,15 +249,17 @@ def collapse_counts(s, *, kv_order: str, S: float, n_sink: int = N_SINK_DEFAULT,
         [1] of which in blocks that contain a sink key (64·b < n_sink)
         [2] unmasked non-sink (i, j) pairs over all blocks
         [3] of which in blocks that contain a sink key
-    The cast operand is computed exactly as in ``online_softmax_pcast``.
+    The cast operand is computed exactly as in ``online_softmax_pcast``; "blocks that
+    contain a sink key" are the 64-key blocks, also when "reverse_sink_last" visits
+    block 0 in two ranges.
     """
     s = np.asarray(s, dtype=np.float64)
     R, N = s.shape
     out = np.zeros(4, dtype=np.int64)
     m = np.full(R, -np.inf)
     keys = np.arange(N)
-    for b in block_visit_order(N, kv_order, block):
-        sb = s[:, b * block:(b + 1) * block]
+    for (j0, j1) in visit_units(N, kv_order, block, n_sink):
+        sb = s[:, j0:j1]
         live = np.isfinite(sb)
         row_live = live.any(axis=1)
         bmax = np.where(live, sb, -np.inf).max(axis=1)
@@ -227,10 +267,10 @@ def collapse_counts(s, *, kv_order: str, S: float, n_sink: int = N_SINK_DEFAULT,
         with np.errstate(invalid="ignore"):
             p = np.where(live, np.exp(sb - m[:, None]), 0.0)
         code = e4m3.encode(p * S)
-        nonsink = (keys[b * block:(b + 1) * block] >= n_sink)[None, :]
+        nonsink = (keys[j0:j1] >= n_sink)[None, :]
         counted = live & nonsink
         zero = counted & (code == 0)
-        sink_block = b * block < n_sink
+        sink_block = (j0 // block) * block < n_sink
         out[0] += int(zero.sum())
         out[2] += int(counted.sum())
         if sink_block:
@@ -249,20 +289,8 @@ def _e4m3_boundaries():
     return vals, mids
 
 
-def _running_max_at_key(s, kv_order, block):
-    R, N = s.shape
-    nb = N // block
-    bmax = np.where(np.isfinite(s), s, -np.inf).reshape(R, nb, block).max(axis=2)
-    run = np.full((R, nb), -np.inf)
-    cur = np.full(R, -np.inf)
-    for b in block_visit_order(N, kv_order, block):
-        cur = np.maximum(cur, bmax[:, b])
-        run[:, b] = cur
-    return np.repeat(run, block, axis=1), cur
-
-
-def _cast_operand(s, kv_order, S, block):
-    m_at_key, m_f = _running_max_at_key(s, kv_order, block)
+def _cast_operand(s, kv_order, S, block, n_sink):
+    m_at_key, m_f = _running_max_at_key(s, kv_order, block, n_sink)
     live = np.isfinite(s)
     with np.errstate(invalid="ignore"):
         x = np.where(live, np.exp(s - m_at_key) * S, 0.0)
@@ -281,7 +309,8 @@ def _codes_near(x, vals, mids):
     return code, other
 
 
-def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_device=None):
+def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_device=None,
+                   n_sink: int = N_SINK_DEFAULT, denominator: str = "fp32"):
     """Per-element extra tolerance where the device may legitimately pick another E4M3 code.
 
     Two sources are covered. (1) A device evaluating P~·S in fp32 (its own exp) may round
@@ -290,19 +319,21 @@ def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_devic
     ``mfma_model``), the device's P~·S follows those logits and its running max, and may
     land on a different code than the exact logits give.
     For every (i, j) the set of admissible codes is: the exact code, the device-logit code,
-    and the neighbour across a midpoint within the window of either value. The allowance
-    of output (i, c) is sum_j max|admissible - exact code value|/S · exp(m_b - m_f) · |v_jc| / l.
+    and the neighbour across a midpoint within the window of either value. With dv_ij the
+    largest |admissible - exact code value| and w_ij = exp(m_u - m_f), the allowance of
+    output (i, c) is sum_j dv_ij · w_ij · |v_jc| / L_i; with the quantized denominator the
+    code also enters L_i, which adds sum_j dv_ij · w_ij · |O_ic| / L_i.
     Returns (allow [R, d], flagged [R, N] bool, zero_flagged [R] int: pairs whose admissible
     codes include both zero and a nonzero code, which can move the collapse count).
     """
     s = np.asarray(s, dtype=np.float64)
-    v = np.abs(np.asarray(v, dtype=np.float64))
+    va = np.abs(np.asarray(v, dtype=np.float64))
     vals, mids = _e4m3_boundaries()
-    x, m_at_key, m_f, live = _cast_operand(s, kv_order, S, block)
+    x, m_at_key, m_f, live = _cast_operand(s, kv_order, S, block, n_sink)
     c0, c1 = _codes_near(x, vals, mids)
     cands = [c0, c1]
     if s_device is not None:
-        xd, _, _, _ = _cast_operand(np.asarray(s_device, dtype=np.float64), kv_order, S, block)
+        xd, _, _, _ = _cast_operand(np.asarray(s_device, dtype=np.float64), kv_order, S, block, n_sink)
         d0, d1 = _codes_near(xd, vals, mids)
         cands += [d0, d1]
     dev = np.zeros_like(x)
@@ -316,9 +347,17 @@ def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_devic
     zero_flag = live & has_zero & has_nonzero
     with np.errstate(invalid="ignore"):
         w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
-        l = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1)
-    weight = np.where(flagged, dev * w, 0.0) / (S * l[:, None])
-    return weight @ v, flagged, zero_flag.sum(axis=1)
+        if denominator == "fp32":
+            L = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1) * S
+        else:
+            L = (np.where(live, vals[c0], 0.0) * w).sum(axis=1)
+    weight = np.where(flagged, dev * w, 0.0) / L[:, None]
+    allow = weight @ va
+    if denominator == "quantized":
+        o = online_softmax_pcast_vectorized(s, v, kv_order=kv_order, S=S, block=block, n_sink=n_sink,
+                                            denominator="quantized")
+        allow = allow + weight.sum(axis=1, keepdims=True) * np.abs(o)
+    return allow, flagged, zero_flag.sum(axis=1)
 
 
 # --------------------------------------------------------------------------------------
@@ -327,7 +366,7 @@ def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_devic
 
 def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str,
                    S: float, rows=None, heads=None, n_sink: int = N_SINK_DEFAULT, logits: str = "exact",
-                   with_allowance: bool = False, with_counts: bool = False):
+                   with_allowance: bool = False, with_counts: bool = False, denominator: str = "fp32"):
     """Oracle over [B, H, N, d] E4M3 inputs (GQA: query head h reads kv head h // (H/Hkv)).
 
     ``q_descale`` is [B, H], ``k_descale``/``v_descale`` are [B, Hkv]. ``rows`` limits the
@@ -342,6 +381,8 @@ def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool,
         of those logits on the row sum and rescaling.
     Returns dict with ``o`` [len(heads), R, d], ``rows``, ``heads`` and, if asked,
     ``allow`` (same shape as o), ``zero_flagged`` and ``counts`` (summed over heads).
+    ``n_sink`` sets the sink tokens of the counts and of "reverse_sink_last";
+    ``denominator`` is "fp32" or "quantized" (see ``online_softmax_pcast``).
     """
     if logits not in ("exact", "device"):
         raise ValueError(logits)
@@ -363,14 +404,15 @@ def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool,
                                             rows=rows, causal=causal)
         s = s_exact if logits == "exact" else s_dev
         vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
-        o, _ = online_softmax_pcast(s, vf, kv_order=kv_order, S=S)
+        opts = {"kv_order": kv_order, "S": S, "n_sink": n_sink, "denominator": denominator}
+        o, _ = online_softmax_pcast(s, vf, **opts)
         outs.append(o)
         if with_allowance:
             if logits == "device":
-                a, _, z = flip_allowance(s_dev, vf, kv_order=kv_order, S=S)
+                a, _, z = flip_allowance(s_dev, vf, **opts)
             else:
-                a, _, z = flip_allowance(s_exact, vf, kv_order=kv_order, S=S, s_device=s_dev)
-                o_dev, _ = online_softmax_pcast(s_dev, vf, kv_order=kv_order, S=S)
+                a, _, z = flip_allowance(s_exact, vf, s_device=s_dev, **opts)
+                o_dev, _ = online_softmax_pcast(s_dev, vf, **opts)
                 a = a + np.abs(o_dev - o)
             allows.append(a)
             zflag += int(z.sum())
