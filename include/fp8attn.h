@@ -30,7 +30,13 @@
  *      finite (decoded value = code value * descale; per-tensor = the same value repeated).
  *  - Grouped-query attention: query head h reads kv head h / (H / Hkv).
  *  - causal != 0 masks key j > query i (equal query and key lengths).
- *  - kv_order: FP8ATTN_KV_FORWARD (0) or FP8ATTN_KV_REVERSE (1).
+ *  - kv_order: FP8ATTN_KV_FORWARD (0), FP8ATTN_KV_REVERSE (1), or, where an entry point
+ *    takes n_sink, FP8ATTN_KV_REVERSE_SINK_LAST (2): the reverse walk with block 0 visited
+ *    in two steps, its non-sink keys [n_sink, 64) first and the sink keys [0, n_sink)
+ *    last (needs n_sink <= 64; n_sink = 0 is plain reverse). This carries the reason the
+ *    technical summary gives for the reverse order (section 2, "Optimization 1": the sink
+ *    should raise m only after every other P has been cast) to the tokens that share
+ *    block 0 with the sinks.
  *  - 0 < S <= 448 (the E4M3 maximum; P~ <= 1 so P~ S never overflows). S = 2^k is exact;
  *    other values are accepted and round like any fp32 multiply.
  *  - stream: a hipStream_t passed as void* (NULL = the default stream). Calls are
@@ -52,15 +58,26 @@ extern "C" {
 typedef enum {
   FP8ATTN_OK = 0,
   FP8ATTN_EINVAL = -1,       /* null pointer, size <= 0, H % Hkv != 0, S not in (0,448],
-                                kv_order/causal not 0/1, n_sink out of [0, N] */
+                                causal not 0/1, kv_order not one the entry point takes,
+                                n_sink out of [0, N] (out of [0, 64] for SINK_LAST),
+                                denominator not 0/1 */
   FP8ATTN_EUNSUPPORTED = -2, /* d not in {64,128,256}, N % 64 != 0, pointer not 16-byte
                                 aligned, grid larger than 2^31-1 workgroups */
   FP8ATTN_ELAUNCH = -3       /* HIP reported an error for the launch */
 } fp8attn_status;
 
-enum { FP8ATTN_KV_FORWARD = 0, FP8ATTN_KV_REVERSE = 1 };
+enum { FP8ATTN_KV_FORWARD = 0, FP8ATTN_KV_REVERSE = 1, FP8ATTN_KV_REVERSE_SINK_LAST = 2 };
 
-/* The forward pass: writes o (every element of [B][H][N][d]). */
+/* What the row sum l accumulates (fp8_attn_fwd_ex):
+ *   FP8ATTN_DENOM_FP32       the unquantized P~ (times S), as in every other entry point;
+ *   FP8ATTN_DENOM_QUANTIZED  the decoded cast operand dec(P8) = dec(E4M3(P~ S)), so that
+ *                            the same quantized P forms numerator and denominator; then
+ *                            O_i = acc / l. The EFQ-Softmax abstract ("EFQ-Softmax:
+ *                            Exp-Free Quantization for Softmax") presents this consistency
+ *                            for its own low-bit P; here it is applied to the E4M3 cast. */
+enum { FP8ATTN_DENOM_FP32 = 0, FP8ATTN_DENOM_QUANTIZED = 1 };
+
+/* The forward pass: writes o (every element of [B][H][N][d]). kv_order 0 or 1. */
 int fp8_attn_fwd(const void* q, const void* k, const void* v, float* o,
                  int B, int H, int Hkv, int N, int d,
                  int causal, int kv_order, float S,
@@ -68,9 +85,10 @@ int fp8_attn_fwd(const void* q, const void* k, const void* v, float* o,
                  void* stream);
 
 /* P-collapse diagnostic: runs the same Q.K^T, running-max, exp and P~ S -> E4M3 path as
- * fp8_attn_fwd (same block order and S; no P.V, no output) and counts, over unmasked
- * pairs (i, j) with key j >= n_sink ("non-sink"), the cast operands that are the E4M3
- * zero. A collapse is a non-sink probability that underflows to zero under the running
+ * fp8_attn_fwd (same block order and S; no P.V, no output; kv_order 0, 1 or 2, where the
+ * sink split of SINK_LAST does not change which blocks count as holding a sink) and
+ * counts, over unmasked pairs (i, j) with key j >= n_sink ("non-sink"), the cast operands
+ * that are the E4M3 zero. A collapse is a non-sink probability that underflows to zero under the running
  * max (technical summary, section 1; the fraction is the F(Delta, S) of section 2).
  *   counts[0]  collapsed non-sink P, all blocks
  *   counts[1]  of which in blocks that contain a sink key (64*b < n_sink)
@@ -92,6 +110,18 @@ int fp8_attn_fwd_counted(const void* q, const void* k, const void* v, float* o,
                          int causal, int kv_order, float S,
                          const float* q_descale, const float* k_descale, const float* v_descale,
                          int n_sink, unsigned long long* counts, void* stream);
+
+/* The forward pass with every option: kv_order 0, 1 or 2 (n_sink sets the sink tokens
+ * of SINK_LAST and of the counts), the row-sum denominator (FP8ATTN_DENOM_*), and counts
+ * either NULL (no diagnostic: o exactly as fp8_attn_fwd_counted would write it) or a
+ * DEVICE pointer to 4 uint64 filled exactly as by fp8_attn_p_collapse_count. With
+ * kv_order 0/1 and FP8ATTN_DENOM_FP32 the results equal those of fp8_attn_fwd and
+ * fp8_attn_fwd_counted. Ownership, alignment and error rules as above. */
+int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
+                    int B, int H, int Hkv, int N, int d,
+                    int causal, int kv_order, float S,
+                    const float* q_descale, const float* k_descale, const float* v_descale,
+                    int n_sink, int denominator, unsigned long long* counts, void* stream);
 
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfp8attn.so")
 
 FP8ATTN_OK = 0
-KV_ORDERS = {"forward": 0, "reverse": 1}
+KV_ORDERS = {"forward": 0, "reverse": 1, "reverse_sink_last": 2}
+DENOMINATORS = {"fp32": 0, "quantized": 1}
 
 _lib = None
 
@@ -27,6 +28,8 @@ def _declare(lib):
     lib.fp8_attn_p_collapse_count.restype = i
     lib.fp8_attn_fwd_counted.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, vp, vp]
     lib.fp8_attn_fwd_counted.restype = i
+    lib.fp8_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i, vp, vp]
+    lib.fp8_attn_fwd_ex.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -165,6 +168,36 @@ def fwd_counted(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv
                                   qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink), counts.data_ptr(),
                                   _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_fwd_counted")
+    return out, counts
+
+
+def fwd_ex(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str = "reverse",
+           S: float = 256.0, n_sink: int = 4, denominator: str = "fp32", count: bool = False,
+           out=None, counts=None, stream=None):
+    """The forward with every option: ``kv_order`` also "reverse_sink_last" (block 0's
+    non-sink keys visited before the n_sink sink tokens), ``denominator`` "fp32" (row sum
+    of P~ S) or "quantized" (row sum of the decoded E4M3 P). With ``count`` (or a
+    ``counts`` tensor) the collapse counts are filled too. Returns (O, counts or None)."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    B, H, Hkv, N, d = _shapes(q8, k8, v8)
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    if counts is None and count:
+        counts = torch.empty(4, dtype=torch.int64, device=dev)
+    rc = lib.fp8_attn_fwd_ex(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                             B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                             qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink), DENOMINATORS[denominator],
+                             None if counts is None else counts.data_ptr(), _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_fwd_ex")
     return out, counts
 
 

@@ -18,7 +18,9 @@ int check_common(int B, int H, int Hkv, int N, int d, int causal, int kv_order, 
   if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FP8ATTN_EINVAL;
   if (H % Hkv != 0) return FP8ATTN_EINVAL;
   if (causal != 0 && causal != 1) return FP8ATTN_EINVAL;
-  if (kv_order != FP8ATTN_KV_FORWARD && kv_order != FP8ATTN_KV_REVERSE) return FP8ATTN_EINVAL;
+  if (kv_order != FP8ATTN_KV_FORWARD && kv_order != FP8ATTN_KV_REVERSE &&
+      kv_order != FP8ATTN_KV_REVERSE_SINK_LAST)
+    return FP8ATTN_EINVAL;
   if (!(S > 0.0f && S <= kE4M3Max)) return FP8ATTN_EINVAL;   // also rejects NaN
   if (d != 64 && d != 128 && d != 256) return FP8ATTN_EUNSUPPORTED;
   if (N % fp8attn::kKvBlock != 0) return FP8ATTN_EUNSUPPORTED;
@@ -48,10 +50,17 @@ void pair_totals(int B, int H, int N, int causal, int n_sink, unsigned long long
   *sink = (uint64_t)B * H * per_head_sink;
 }
 
+// n_sink for the counts and the sink split: within [0, N], and at most one block when
+// block 0 is split.
+bool n_sink_ok(int n_sink, int N, int kv_order) {
+  if (n_sink < 0 || n_sink > N) return false;
+  return kv_order != FP8ATTN_KV_REVERSE_SINK_LAST || n_sink <= fp8attn::kKvBlock;
+}
+
 fp8attn::Params make_params(const void* q, const void* k, const void* v, float* o,
                             int B, int H, int Hkv, int N, int d, int causal, int kv_order,
                             float S, const float* qd, const float* kd, const float* vd,
-                            int n_sink, unsigned long long* counts) {
+                            int n_sink, unsigned long long* counts, int denominator = FP8ATTN_DENOM_FP32) {
   fp8attn::Params p{};
   p.q = static_cast<const uint8_t*>(q);
   p.k = static_cast<const uint8_t*>(k);
@@ -63,13 +72,14 @@ fp8attn::Params make_params(const void* q, const void* k, const void* v, float* 
   p.counts = counts;
   p.B = B; p.H = H; p.Hkv = Hkv; p.N = N;
   p.causal = causal;
-  p.reverse = kv_order == FP8ATTN_KV_REVERSE;
+  p.reverse = kv_order != FP8ATTN_KV_FORWARD;
   p.n_sink = n_sink;
+  p.sink_last = kv_order == FP8ATTN_KV_REVERSE_SINK_LAST && n_sink > 0;
+  p.qden = denominator == FP8ATTN_DENOM_QUANTIZED;
   p.S = S;
   int e2 = 0;
-  const float mant = frexpf(S, &e2);
+  frexpf(S, &e2);                       // S = 2^k gives a mantissa of 1/2 and e2 = k + 1
   p.log2_S = (float)(e2 - 1);
-  (void)mant;
   p.log2e_rsqrt_d = (float)(1.4426950408889634 / sqrt((double)d));
   if (counts) pair_totals(B, H, N, causal, n_sink, &p.pairs, &p.pairs_sink);
   return p;
@@ -90,6 +100,7 @@ int fp8_attn_fwd(const void* q, const void* k, const void* v, float* o,
                  const float* q_descale, const float* k_descale, const float* v_descale,
                  void* stream) {
   if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale) return FP8ATTN_EINVAL;
+  if (kv_order == FP8ATTN_KV_REVERSE_SINK_LAST) return FP8ATTN_EINVAL;   // needs n_sink
   const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
   if (st != FP8ATTN_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FP8ATTN_EUNSUPPORTED;
@@ -107,7 +118,7 @@ int fp8_attn_p_collapse_count(const void* q, const void* k,
   if (!q || !k || !q_descale || !k_descale || !counts) return FP8ATTN_EINVAL;
   const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
   if (st != FP8ATTN_OK) return st;
-  if (n_sink < 0 || n_sink > N) return FP8ATTN_EINVAL;
+  if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k)) return FP8ATTN_EUNSUPPORTED;
   const fp8attn::Params p = make_params(q, k, nullptr, nullptr, B, H, Hkv, N, d, causal, kv_order, S,
                                         q_descale, k_descale, nullptr, n_sink, counts);
@@ -123,7 +134,7 @@ int fp8_attn_fwd_counted(const void* q, const void* k, const void* v, float* o,
   if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale || !counts) return FP8ATTN_EINVAL;
   const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
   if (st != FP8ATTN_OK) return st;
-  if (n_sink < 0 || n_sink > N) return FP8ATTN_EINVAL;
+  if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FP8ATTN_EUNSUPPORTED;
   const fp8attn::Params p = make_params(q, k, v, o, B, H, Hkv, N, d, causal, kv_order, S,
                                         q_descale, k_descale, v_descale, n_sink, counts);
@@ -131,9 +142,28 @@ int fp8_attn_fwd_counted(const void* q, const void* k, const void* v, float* o,
   return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
 }
 
+int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
+                    int B, int H, int Hkv, int N, int d,
+                    int causal, int kv_order, float S,
+                    const float* q_descale, const float* k_descale, const float* v_descale,
+                    int n_sink, int denominator, unsigned long long* counts, void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
+  if (denominator != FP8ATTN_DENOM_FP32 && denominator != FP8ATTN_DENOM_QUANTIZED) return FP8ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FP8ATTN_EUNSUPPORTED;
+  const fp8attn::Params p = make_params(q, k, v, o, B, H, Hkv, N, d, causal, kv_order, S,
+                                        q_descale, k_descale, v_descale, n_sink, counts, denominator);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool pow2 = is_pow2(S);
+  const hipError_t e = counts ? fp8attn::launch_fwd_count(p, d, pow2, s) : fp8attn::launch_fwd(p, d, pow2, s);
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
 int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
 
-const char* fp8_attn_version(void) { return "fp8attn-gfx950 0.1.0"; }
+const char* fp8_attn_version(void) { return "fp8attn-gfx950 0.2.0"; }
 
 const char* fp8_attn_status_string(int status) {
   switch (status) {

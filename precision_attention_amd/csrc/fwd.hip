@@ -292,17 +292,25 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
   // ---- online softmax of block blk with scores s: running max and sum, the rescale of O,
   // the E4M3 cast of P (into pop, the B-operand layout of the P.V product) and the counts
-  auto softmax = [&](f32x16 (&s)[2], int blk, i32x8& pop) __attribute__((always_inline)) {
-    // causal mask (key j > query i) on the wave's diagonal block (blocks past it are
-    // never visited; the test covers them too)
-    if (p.causal && blk >= diag) {
-      // element (t, r) holds key blk * 64 + 4 half + k with k = 32t + 8(r / 4) + r % 4
-      const int rel = i_row - blk * kKvBlock - 4 * half;
+  // part: 0 = the whole block; with the sink split of block 0, 1 = its non-sink keys
+  // [n_sink, 64) and 2 = its sink keys [0, n_sink)
+  auto softmax = [&](f32x16 (&s)[2], int blk, i32x8& pop, int part) __attribute__((always_inline)) {
+    // Masking: causal (key j > query i) on the wave's diagonal block (blocks past it are
+    // never visited; the test covers them too), and the key window of a split part.
+    if ((p.causal && blk >= diag) || part != 0) {
+      // keep key offsets lo..hi within the block; element (t, r) holds offset
+      // 32t + 8(r / 4) + r % 4 + 4 half
+      int hi = p.causal ? min(i_row - blk * kKvBlock, kKvBlock - 1) : kKvBlock - 1;
+      if (part == 2) hi = min(hi, p.n_sink - 1);
+      const int lo = part == 1 ? p.n_sink : 0;
+      const int hi_rel = hi - 4 * half, lo_rel = lo - 4 * half;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + (r & 3) > rel) s[t][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int k = 32 * t + 8 * (r >> 2) + (r & 3);
+          if (k > hi_rel || k < lo_rel) s[t][r] = -INFINITY;
+        }
     }
 
     // running max: raw maximum, scaled once (c > 0 keeps the order)
@@ -341,9 +349,19 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
         pw[4 * t + a] = w;
       }
+    if (p.qden) {
+      // row sum of the decoded cast operand: codes back to fp32 (exact), two per cvt
+      lsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pw[q], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pw[q], true);
+        lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
+    }
     l_run = alpha * l_run + lsum;
 
-    if (CNT) {
+    if (CNT && part != 2) {   // the sink keys themselves are never counted
       // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
       // carries and leaves bit 7 clear exactly for a zero code.
       const int jb = blk * kKvBlock;
@@ -421,15 +439,21 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         if (OUT) dma_tile(Vg, block_of(n + 1), vbuf(cur ^ 1));
       }
       if (active(n)) {
-        f32x16 s[2];
-        qk(kbuf(cur), s);
-        i32x8 vpre[NVARR];
-        if (OUT) {
+        const int blk = block_of(n);
+        // one visit, or two for block 0 under the sink split (its non-sink keys first)
+        const bool split = p.sink_last && blk == 0;
+        const int last_part = split ? 2 : 0;
+        for (int part = split ? 1 : 0; part <= last_part; ++part) {
+          f32x16 s[2];
+          qk(kbuf(cur), s);
+          i32x8 vpre[NVARR];
+          if (OUT) {
 #pragma unroll
-          for (int u = 0; u < NVPRE; ++u) vpre[u] = read_v(vbuf(cur), u);
+            for (int u = 0; u < NVPRE; ++u) vpre[u] = read_v(vbuf(cur), u);
+          }
+          softmax(s, blk, pop, part);
+          if (OUT) pv(vbuf(cur), pop, vpre);
         }
-        softmax(s, block_of(n), pop);
-        if (OUT) pv(vbuf(cur), pop, vpre);
       }
       dma_wait_sync();
     };

@@ -19,6 +19,8 @@ struct Params {
   unsigned long long pairs_sink;    // of which in KV blocks holding a sink token
   int B, H, Hkv, N;
   int causal, reverse, n_sink;
+  int sink_last;                    // reverse walk, block 0 as [n_sink, 64) then [0, n_sink)
+  int qden;                         // row sum of the decoded cast operand (else of P~ S)
   float S;                          // static P scale
   float log2_S;                     // exact log2(S) when S is a power of two
   float log2e_rsqrt_d;              // log2(e)/sqrt(d), rounded once to fp32

@@ -41,11 +41,12 @@ def gpu_counts(t, *, causal, order, S, n_sink=4):
     return c.cpu().numpy().astype(np.int64)
 
 
-def oracle(inp, *, causal, order, S, rows=None, heads=None, counts=False, n_sink=4, logits="device"):
+def oracle(inp, *, causal, order, S, rows=None, heads=None, counts=False, n_sink=4, logits="device",
+           denominator="fp32"):
     return oracle_attention.attention_e4m3(inp["q8"], inp["k8"], inp["v8"], inp["qd"], inp["kd"], inp["vd"],
                                            causal=causal, kv_order=order, S=S, rows=rows, heads=heads,
                                            n_sink=n_sink, logits=logits, with_allowance=True,
-                                           with_counts=counts)
+                                           with_counts=counts, denominator=denominator)
 
 
 def check_output(o_gpu, ref, label=""):
@@ -69,16 +70,18 @@ def check_counts(c_gpu, c_ref, zero_flagged, label=""):
         assert abs(int(c_gpu[i]) - int(c_ref[i])) <= slack, f"count[{i}] differs"
 
 
-def check_both(inp, o, c, *, causal, order, S, label, rows=None, heads=None, count_heads=None):
+def check_both(inp, o, c, *, causal, order, S, label, rows=None, heads=None, count_heads=None, n_sink=4,
+               denominator="fp32"):
     """Tight check against the oracle on the device's matrix-core logits, then the check
     against the exact-logit oracle with its wider (matrix-core aware) tolerance."""
+    opts = {"n_sink": n_sink, "denominator": denominator}
     for logits in ("device", "exact"):
         ref = oracle(inp, causal=causal, order=order, S=S, rows=rows, heads=heads, logits=logits,
-                     counts=c is not None and count_heads is None)
+                     counts=c is not None and count_heads is None, **opts)
         check_output(o, ref, f"{label} [{logits} logits]")
         if c is not None:
             cref = ref if count_heads is None else oracle(inp, causal=causal, order=order, S=S, heads=count_heads,
-                                                          logits=logits, counts=True)
+                                                          logits=logits, counts=True, **opts)
             check_counts(c, cref["counts"], cref["zero_flagged"], f"{label} [{logits} logits]")
 
 

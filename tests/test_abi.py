@@ -92,6 +92,29 @@ def test_fwd_counted_validation(lib, kw, status):
     assert rc == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), -1), (dict(v=None), -1), (dict(n_sink=-1), -1), (dict(n_sink=129), -1),
+    (dict(order=2, n_sink=65), -1), (dict(order=3), -1), (dict(denominator=2), -1),
+    (dict(denominator=-1), -1), (dict(S=0.0), -1), (dict(causal=5), -1),
+    (dict(d=80), -2), (dict(N=200), -2), (dict(o=FAKE + 4), -2),
+])
+def test_fwd_ex_validation(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=2, S=256.0,
+             qd=FAKE, kd=FAKE, vd=FAKE, n_sink=4, denominator=1, counts=None)
+    a.update(kw)
+    rc = lib.fp8_attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                             a["causal"], a["order"], a["S"], a["qd"], a["kd"], a["vd"], a["n_sink"],
+                             a["denominator"], a["counts"], None)
+    assert rc == status
+
+
+def test_sink_last_needs_an_entry_point_with_n_sink(lib):
+    assert _fwd(lib, order=2) == -1
+    # the counting entry points take it (validation passes up to the n_sink bound)
+    rc = lib.fp8_attn_p_collapse_count(FAKE, FAKE, 1, 2, 1, 128, 128, 1, 2, 256.0, FAKE, FAKE, 65, FAKE, None)
+    assert rc == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 
