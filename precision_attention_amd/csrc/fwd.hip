@@ -116,7 +116,9 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, int range, uint8_
 #endif
 
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
-template <int D, bool POW2, bool OUT, bool CNT>
+// EXT: the options of fp8_attn_fwd_ex (sink split of block 0, quantized row sum); the
+// launches without them run the kernel compiled without their branches.
+template <int D, bool POW2, bool OUT, bool CNT, bool EXT>
 __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_kernel(const Params p) {
   constexpr int kWaves = waves_for(D);
   constexpr int kThreads = 64 * kWaves;
@@ -297,12 +299,12 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   auto softmax = [&](f32x16 (&s)[2], int blk, i32x8& pop, int part) __attribute__((always_inline)) {
     // Masking: causal (key j > query i) on the wave's diagonal block (blocks past it are
     // never visited; the test covers them too), and the key window of a split part.
-    if ((p.causal && blk >= diag) || part != 0) {
+    if ((p.causal && blk >= diag) || (EXT && part != 0)) {
       // keep key offsets lo..hi within the block; element (t, r) holds offset
       // 32t + 8(r / 4) + r % 4 + 4 half
       int hi = p.causal ? min(i_row - blk * kKvBlock, kKvBlock - 1) : kKvBlock - 1;
-      if (part == 2) hi = min(hi, p.n_sink - 1);
-      const int lo = part == 1 ? p.n_sink : 0;
+      if (EXT && part == 2) hi = min(hi, p.n_sink - 1);
+      const int lo = EXT && part == 1 ? p.n_sink : 0;
       const int hi_rel = hi - 4 * half, lo_rel = lo - 4 * half;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -349,7 +351,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
         pw[4 * t + a] = w;
       }
-    if (p.qden) {
+    if (EXT && p.qden) {
       // row sum of the decoded cast operand: codes back to fp32 (exact), two per cvt
       lsum = 0.f;
 #pragma unroll
@@ -361,7 +363,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     }
     l_run = alpha * l_run + lsum;
 
-    if (CNT && part != 2) {   // the sink keys themselves are never counted
+    if (CNT && !(EXT && part == 2)) {   // the sink keys themselves are never counted
       // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
       // carries and leaves bit 7 clear exactly for a zero code.
       const int jb = blk * kKvBlock;
@@ -441,7 +443,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
       if (active(n)) {
         const int blk = block_of(n);
         // one visit, or two for block 0 under the sink split (its non-sink keys first)
-        const bool split = p.sink_last && blk == 0;
+        const bool split = EXT && p.sink_last && blk == 0;
         const int last_part = split ? 2 : 0;
         for (int part = split ? 1 : 0; part <= last_part; ++part) {
           f32x16 s[2];
@@ -522,6 +524,7 @@ __global__ void init_counts_kernel(unsigned long long* counts, unsigned long lon
 
 template <bool OUT, bool CNT>
 hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
+  const bool ext = p.sink_last || p.qden;
   if (CNT) {
     hipLaunchKernelGGL(init_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts, p.pairs, p.pairs_sink);
     const hipError_t e = hipGetLastError();
@@ -530,8 +533,13 @@ hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
 #define FP8ATTN_LAUNCH(D)                                                                       \
   {                                                                                             \
     const dim3 grid((unsigned)num_workgroups(p, D)), block(64 * waves_for(D));                  \
-    if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT>), grid, block, 0, stream, p);  \
-    else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT>), grid, block, 0, stream, p);      \
+    if (ext) {                                                                                  \
+      if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT, true>), grid, block, 0, stream, p); \
+      else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT, true>), grid, block, 0, stream, p);     \
+    } else {                                                                                    \
+      if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT, false>), grid, block, 0, stream, p); \
+      else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT, false>), grid, block, 0, stream, p);     \
+    }                                                                                           \
   }
   switch (d) {
     case 64: FP8ATTN_LAUNCH(64) break;
