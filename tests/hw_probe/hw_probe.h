@@ -22,6 +22,18 @@ int hw_probe_cvt_e4m3(const float* in, unsigned char* out, long n, void* stream)
 int hw_probe_mfma_dots(const unsigned char* a, const unsigned char* b, float* raw, int T, int kch,
                        void* stream);
 
+/* Throughput kernel for the roofline denominators. Each of `blocks` workgroups of 512
+ * threads (8 waves, 2 per SIMD) runs `iters` iterations of
+ *   kind 0: 8 v_mfma_f32_32x32x64_f8f6f4 on 4 independent accumulators (131072 FLOP each);
+ *   kind 1: 32 v_exp_f32, each followed by one v_sub_f32 that keeps the chain bounded;
+ *   kind 2: both in the same wave;
+ *   kind 3: waves 0-3 the MFMA part, waves 4-7 the exp part (split across waves).
+ * sink[blocks*512] receives one float per thread (so no work is dead code). clock[blocks]
+ * receives, per workgroup, shader-clock ticks per 100 MHz real-time tick measured over the
+ * loop by wave 0 (s_memtime / s_memrealtime); multiply by 1e8 for Hz. seed: 256 ints. */
+int hw_probe_throughput(int kind, int blocks, int iters, const int* seed, float* sink, float* clock,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,59 @@ __global__ void mfma_kernel(const uint8_t* a, const uint8_t* b, float* raw, int 
   }
 }
 
+__global__ __launch_bounds__(512) void throughput_kernel(int kind, int iters, const int* seed, float* sink,
+                                                         float* clock) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  i32x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = seed[(tid + i) & 255] & 0x3f3f3f3f;
+    b[i] = seed[(tid + 3 * i) & 255] & 0x3f3f3f3f;
+  }
+  f32x16 acc[4];
+  for (int u = 0; u < 4; ++u) acc[u] = f32x16{0};
+  float x[32];
+  for (int i = 0; i < 32; ++i) x[i] = (float)(seed[(tid + 7 * i) & 255] & 1023) * 1e-3f - 20.f;
+  bool do_m = kind == 0 || kind == 2, do_e = kind == 1 || kind == 2;
+  if (kind == 3) {
+    do_m = wave < 4;
+    do_e = wave >= 4;
+  }
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    if (do_m) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[u], 0, 0, 0, 0, 0, 0);
+    }
+    if (do_e) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]) - 20.f;
+    }
+  }
+  float s = 0.f;
+  for (int u = 0; u < 4; ++u)
+    for (int r = 0; r < 16; ++r) s += acc[u][r];
+  for (int i = 0; i < 32; ++i) s += x[i];
+  sink[(size_t)blockIdx.x * blockDim.x + tid] = s;
+  if (tid == 0) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clock[blockIdx.x] = r1 > r0 ? (float)((double)(t1 - t0) / (double)(r1 - r0)) : 0.f;
+  }
+}
+
 }  // namespace
+
+extern "C" int hw_probe_throughput(int kind, int blocks, int iters, const int* seed, float* sink, float* clock,
+                                   void* stream) {
+  if (kind < 0 || kind > 3 || blocks <= 0 || iters <= 0 || !seed || !sink || !clock) return -1;
+  hipLaunchKernelGGL(throughput_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, kind, iters, seed,
+                     sink, clock);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int hw_probe_cvt_e4m3(const float* in, unsigned char* out, long n, void* stream) {
   if (!in || !out || n <= 0 || (n & 1)) return -1;

@@ -30,6 +30,7 @@ def probe():
     vp = ctypes.c_void_p
     lib.hw_probe_cvt_e4m3.argtypes = [vp, vp, ctypes.c_long, vp]
     lib.hw_probe_mfma_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.hw_probe_throughput.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
     return lib
 
 
@@ -88,3 +89,39 @@ def test_hardware_mfma_matches_accumulation_model(probe, kch):
         f"max|hw-exact| {np.abs(hw - exact).max():.3g}")
     assert same.mean() >= 0.999
     assert (np.abs(hw - model) <= ulp).all()
+
+
+def test_throughput_roofline_denominators(probe):
+    """The measured ceilings the kernel's roofline fraction is read against: the FP8
+    matrix-core rate of a pure v_mfma_f32_32x32x64_f8f6f4 stream, the v_exp_f32 rate, how
+    far the two overlap (same wave, and split across the two waves of a SIMD), and the
+    shader clock they ran at (printed; loose sanity bounds only)."""
+    dev = device()
+    blocks, iters = 1024, 2000
+    seed = torch.from_numpy(np.random.default_rng(0).integers(0, 2**31 - 1, 256).astype(np.int32)).to(dev)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    clock = torch.empty(blocks, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for kind, name in ((0, "mfma"), (1, "exp"), (2, "mfma+exp same wave"), (3, "mfma | exp split waves")):
+        for rep in range(2):      # first launch warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert probe.hw_probe_throughput(kind, blocks, iters, seed.data_ptr(), sink.data_ptr(),
+                                             clock.data_ptr(), ctypes.c_void_p(stream.cuda_stream)) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        ghz = float(clock.median()) * 0.1
+        waves = blocks * 8 * (0.5 if kind == 3 else 1.0)
+        flop = waves * iters * 8 * 2 * 32 * 32 * 64 if kind != 1 else 0.0
+        exps = blocks * 8 * (0.5 if kind == 3 else 1.0) * iters * 32 * 64 if kind != 0 else 0.0
+        tflops, texp = flop / ms / 1e9, exps / ms / 1e9
+        res[name] = (ms, tflops, texp, ghz)
+        per_clk = f"{flop / (ms * 1e-3) / (ghz * 1e9) / 1024:.0f} FLOP/clk/SIMD" if flop else \
+            f"{exps / (ms * 1e-3) / (ghz * 1e9) / 256:.1f} exp/clk/CU"
+        say(f"  {name:24s} {ms:8.3f} ms  {tflops:8.1f} TFLOP/s  {texp:6.2f} Texp/s  clock {ghz:.2f} GHz  {per_clk}")
+    assert 1.0 < res["mfma"][3] < 2.7
+    assert res["mfma"][1] > 2000.0              # FP8 MFMA stream well above 40% of 5.0 PF
+    # the exp work hides under the MFMA work when both come from the same wave
+    assert res["mfma+exp same wave"][0] < 1.5 * res["mfma"][0]
