@@ -39,6 +39,11 @@ Two variants beyond the pages' own two choices (order, S), each an option here:
     P~·S, so that the same quantized P feeds the numerator and the denominator (the
     consistency idea of the EFQ-Softmax abstract, applied to the E4M3 cast); then
     O = acc / l.
+And one more workload shape: decode (one query row per head over all N keys) with the key
+range split into contiguous ranges. Each split runs the recurrence above on its own keys
+(its own running max, its blocks in the chosen order), and the split states are merged
+exactly through their maxima, as FlashAttention-style split-KV does. The P cast therefore
+depends on the split, and the oracle reproduces that partition.
 
 Everything is fp64. Q·K^T is taken over the raw decoded E4M3 values, which is exact
 in fp64 (every product is a multiple of 2^-18 and every partial sum stays far below
@@ -358,6 +363,104 @@ def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_devic
                                             denominator="quantized")
         allow = allow + weight.sum(axis=1, keepdims=True) * np.abs(o)
     return allow, flagged, zero_flag.sum(axis=1)
+
+
+# --------------------------------------------------------------------------------------
+# decode with the key range split (one query row per head)
+# --------------------------------------------------------------------------------------
+
+def split_ranges(n_keys: int, n_split: int, block: int = BLOCK):
+    """The contiguous key ranges of a split-KV pass: the nb = n_keys / 64 blocks shared as
+    evenly as possible, split s holding blocks [floor(s nb / n), floor((s + 1) nb / n))."""
+    nb = n_keys // block
+    if not 1 <= n_split <= nb:
+        raise ValueError("need 1 <= n_split <= number of blocks")
+    return [((s * nb // n_split) * block, ((s + 1) * nb // n_split) * block) for s in range(n_split)]
+
+
+def online_softmax_state(s, v, *, kv_order: str, S: float, p_cast: str = "e4m3", block: int = BLOCK):
+    """The recurrence of ``online_softmax_pcast`` over the keys of ``s`` (one split), returned
+    unnormalised: (m [R], l [R], acc [R, d]) with l = sum of P~·S and acc = sum P8·v, both
+    relative to the final max m of this split."""
+    s = np.asarray(s, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    R, N = s.shape
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, v.shape[1]))
+    for (j0, j1) in visit_units(N, kv_order, block, 0):
+        sb = s[:, j0:j1]
+        live = np.isfinite(sb)
+        row_live = live.any(axis=1)
+        bmax = np.where(live, sb, -np.inf).max(axis=1)
+        m_new = np.where(row_live, np.maximum(m, bmax), m)
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+            p = np.where(live, np.exp(sb - m_new[:, None]), 0.0)
+        p8 = _cast(p * S, p_cast)
+        l = alpha * l + p.sum(axis=1) * S
+        acc = alpha[:, None] * acc + p8 @ v[j0:j1]
+        m = m_new
+    return m, l, acc
+
+
+def decode_split(s, v, *, kv_order: str, S: float, n_split: int, p_cast: str = "e4m3", block: int = BLOCK):
+    """Split-KV decode: every split runs the online softmax with the P-cast over its own key
+    range (its own running max, its blocks in ``kv_order``); the split states are then merged
+    exactly: with m = max_s m_s, O = sum_s acc_s e^(m_s - m) / sum_s l_s e^(m_s - m)."""
+    parts = [online_softmax_state(s[:, j0:j1], v[j0:j1], kv_order=kv_order, S=S, p_cast=p_cast, block=block)
+             for (j0, j1) in split_ranges(s.shape[1], n_split, block)]
+    m = np.max(np.stack([p[0] for p in parts]), axis=0)
+    num = sum(np.exp(p[0] - m)[:, None] * p[2] for p in parts)
+    den = sum(np.exp(p[0] - m) * p[1] for p in parts)
+    return num / den[:, None]
+
+
+def decode_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str, S: float, n_split: int,
+                logits: str = "exact", with_allowance: bool = False):
+    """Decode oracle over E4M3 inputs: q8 [B, H, d] (one query row per head), k8/v8
+    [B, Hkv, N, d]; every query sees all N keys. Returns dict with ``o`` [B, H, d] and,
+    if asked, ``allow`` (the rounding-boundary allowance of ``flip_allowance`` evaluated on
+    each split, plus |O(device logits) - O(exact logits)| for exact logits)."""
+    B, H, d = q8.shape
+    Hkv = k8.shape[1]
+    group = H // Hkv
+    o = np.zeros((B, H, d))
+    allow = np.zeros((B, H, d))
+    for b in range(B):
+        for h in range(H):
+            hk = h // group
+            qrow = q8[b, h][None, :]
+            s_exact, _ = head_logits_e4m3(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+            s_dev = None
+            if logits == "device" or with_allowance:
+                s_dev = mfma_model.model_logits(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+            s = s_exact if logits == "exact" else s_dev
+            vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
+            o[b, h] = decode_split(s, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
+            if with_allowance:
+                a = np.zeros(d)
+                parts = split_ranges(s.shape[1], n_split)
+                # each split's own allowance, weighted by the share of the merged row sum it holds
+                states = [online_softmax_state(s[:, j0:j1], vf[j0:j1], kv_order=kv_order, S=S)
+                          for (j0, j1) in parts]
+                m = max(st[0][0] for st in states)
+                den = sum(np.exp(st[0][0] - m) * st[1][0] for st in states)
+                for (j0, j1), st in zip(parts, states):
+                    kw = {"kv_order": kv_order, "S": S, "n_sink": 0}
+                    if logits == "device":
+                        a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], **kw)
+                    else:
+                        a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], s_device=s_dev[:, j0:j1], **kw)
+                    a += a_s[0] * np.exp(st[0][0] - m) * st[1][0] / den
+                if logits == "exact":
+                    o_dev = decode_split(s_dev, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
+                    a += np.abs(o_dev - o[b, h])
+                allow[b, h] = a
+    res = {"o": o}
+    if with_allowance:
+        res["allow"] = allow
+    return res
 
 
 # --------------------------------------------------------------------------------------
