@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 METRIC = "FP8 attn fwd TFLOP/s (causal, d=128) + %MFMA peak; P-collapse frac & MSE"
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 matrix peak (no sparsity)
 DEFAULT_WORKLOAD = "gqa_causal_h32_kv8_n32768_d128"
-KERNEL_SOURCES = ["precision_attention_amd/csrc/fwd.hip", "precision_attention_amd/csrc/launch.h"]
+KERNEL_SOURCES = ["precision_attention_amd/csrc/fwd.hip", "precision_attention_amd/csrc/launch.h",
+                  "precision_attention_amd/csrc/kernel_common.h"]
 
 
 def log(msg):
@@ -163,6 +164,8 @@ def main():
     from precision_attention_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
+    if w.decode:
+        return bench_decode(args, w)
     dev = torch.device("cuda:0")
     log(f"bench: generating {w.name} (seed {args.seed})")
     inp = I.make_workload_inputs(w, seed=args.seed, keep_float=not args.no_quality)
@@ -241,6 +244,53 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(inp, w, args.order, args.S, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, w):
+    """Split-KV decode (one query row per head over all N keys): HBM-bound, so the roofline
+    is the HBM peak against the algorithmic bytes (Q, K, V once, O once)."""
+    import numpy as np
+    import torch
+
+    from precision_attention_amd import binding
+    from precision_attention_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {w.name} (seed {args.seed})")
+    inp = I.make_workload_inputs(w, seed=args.seed, keep_float=False)
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev) for k in ("q8", "k8", "v8", "qd", "kd", "vd")}
+    n_split = binding.decode_default_splits(w.B, w.Hkv, w.H, w.N)
+    o = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.load().fp8_attn_decode_workspace_bytes(w.B, w.H, w.d, n_split), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], kv_order=args.order, S=args.S,
+                       n_split=n_split, out=o, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = w.bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"metric": "FP8 P-cast split-KV decode, algorithmic GB/s (Q, K, V, O once)", "value": gbs,
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                      "kv_order": args.order, "S": args.S, "n_split": n_split, "delta": w.delta},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
+                        "traffic": None, "kernel": "decode_kernel<128,pow2> + decode_merge_kernel",
+                        "bytes_per_launch": nbytes},
+           "tflops": w.flop() / (ms * 1e-3) / 1e12}
     print(json.dumps(out), flush=True)
 
 

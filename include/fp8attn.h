@@ -61,8 +61,9 @@ typedef enum {
                                 causal not 0/1, kv_order not one the entry point takes,
                                 n_sink out of [0, N] (out of [0, 64] for SINK_LAST),
                                 denominator not 0/1 */
-  FP8ATTN_EUNSUPPORTED = -2, /* d not in {64,128,256}, N % 64 != 0, pointer not 16-byte
-                                aligned, grid larger than 2^31-1 workgroups */
+  FP8ATTN_EUNSUPPORTED = -2, /* d not in {64,128,256}, N % 64 != 0, N*d > 2^31-1,
+                                pointer not 16-byte aligned, grid larger than 2^31-1
+                                workgroups */
   FP8ATTN_ELAUNCH = -3       /* HIP reported an error for the launch */
 } fp8attn_status;
 
@@ -122,6 +123,30 @@ int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
                     int causal, int kv_order, float S,
                     const float* q_descale, const float* k_descale, const float* v_descale,
                     int n_sink, int denominator, unsigned long long* counts, void* stream);
+
+/* Decode with the key range split (one query row per head, every query sees all N keys).
+ * The N / 64 KV blocks are shared into n_split contiguous ranges (split s holds blocks
+ * [floor(s nb / n_split), floor((s+1) nb / n_split)), 1 <= n_split <= N / 64). Each split
+ * runs the online softmax with the P-cast above over its own keys -- its own running max,
+ * its blocks in kv_order (0 or 1), S as above -- and the split states (m, l, acc) are
+ * merged exactly through their maxima: with m = max_s m_s,
+ *   O = sum_s acc_s e^(m_s - m) / (S sum_s l_s e^(m_s - m)),
+ * the split-KV form of the FlashAttention recurrence the technical summary's section 1
+ * describes. The cast depends on the partition (a split that does not hold the sink
+ * tokens never sees their max).
+ *   q  [B][H][d] uint8 E4M3, k, v [B][Hkv][N][d], o [B][H][d] float32 (written);
+ *   q_descale [B*H], k_descale and v_descale [B*Hkv];
+ *   workspace: DEVICE buffer of at least fp8_attn_decode_workspace_bytes(B, H, d, n_split)
+ *   bytes, 16-byte aligned, owned by the caller; its contents on entry do not matter and
+ *   on return are unspecified. Calls sharing one workspace must not overlap in time.
+ * Errors as above (EINVAL also for a workspace that is NULL or too small, or n_split out
+ * of range; EUNSUPPORTED for d not in {64,128,256}, N % 64 != 0 or a misaligned pointer).
+ * Two kernels are enqueued on `stream`: the split pass and the merge. */
+unsigned long long fp8_attn_decode_workspace_bytes(int B, int H, int d, int n_split);
+int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
+                    int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                    const float* q_descale, const float* k_descale, const float* v_descale,
+                    int n_split, void* workspace, unsigned long long workspace_bytes, void* stream);
 
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);

@@ -417,46 +417,48 @@ def decode_split(s, v, *, kv_order: str, S: float, n_split: int, p_cast: str = "
 
 
 def decode_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str, S: float, n_split: int,
-                logits: str = "exact", with_allowance: bool = False):
+                logits: str = "exact", with_allowance: bool = False, heads=None):
     """Decode oracle over E4M3 inputs: q8 [B, H, d] (one query row per head), k8/v8
-    [B, Hkv, N, d]; every query sees all N keys. Returns dict with ``o`` [B, H, d] and,
-    if asked, ``allow`` (the rounding-boundary allowance of ``flip_allowance`` evaluated on
-    each split, plus |O(device logits) - O(exact logits)| for exact logits)."""
+    [B, Hkv, N, d]; every query sees all N keys. ``heads``: optional list of (b, h) to
+    compute (the others stay 0). Returns dict with ``o`` [B, H, d] and, if asked, ``allow``
+    (the rounding-boundary allowance of ``flip_allowance`` evaluated on each split, plus
+    |O(device logits) - O(exact logits)| for exact logits)."""
     B, H, d = q8.shape
     Hkv = k8.shape[1]
     group = H // Hkv
     o = np.zeros((B, H, d))
     allow = np.zeros((B, H, d))
-    for b in range(B):
-        for h in range(H):
-            hk = h // group
-            qrow = q8[b, h][None, :]
-            s_exact, _ = head_logits_e4m3(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
-            s_dev = None
-            if logits == "device" or with_allowance:
-                s_dev = mfma_model.model_logits(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
-            s = s_exact if logits == "exact" else s_dev
-            vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
-            o[b, h] = decode_split(s, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
-            if with_allowance:
-                a = np.zeros(d)
-                parts = split_ranges(s.shape[1], n_split)
-                # each split's own allowance, weighted by the share of the merged row sum it holds
-                states = [online_softmax_state(s[:, j0:j1], vf[j0:j1], kv_order=kv_order, S=S)
-                          for (j0, j1) in parts]
-                m = max(st[0][0] for st in states)
-                den = sum(np.exp(st[0][0] - m) * st[1][0] for st in states)
-                for (j0, j1), st in zip(parts, states):
-                    kw = {"kv_order": kv_order, "S": S, "n_sink": 0}
-                    if logits == "device":
-                        a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], **kw)
-                    else:
-                        a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], s_device=s_dev[:, j0:j1], **kw)
-                    a += a_s[0] * np.exp(st[0][0] - m) * st[1][0] / den
-                if logits == "exact":
-                    o_dev = decode_split(s_dev, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
-                    a += np.abs(o_dev - o[b, h])
-                allow[b, h] = a
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in heads:
+        hk = h // group
+        qrow = q8[b, h][None, :]
+        s_exact, _ = head_logits_e4m3(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+        s_dev = None
+        if logits == "device" or with_allowance:
+            s_dev = mfma_model.model_logits(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+        s = s_exact if logits == "exact" else s_dev
+        vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
+        o[b, h] = decode_split(s, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
+        if with_allowance:
+            a = np.zeros(d)
+            parts = split_ranges(s.shape[1], n_split)
+            # each split's own allowance, weighted by the share of the merged row sum it holds
+            states = [online_softmax_state(s[:, j0:j1], vf[j0:j1], kv_order=kv_order, S=S)
+                      for (j0, j1) in parts]
+            m = max(st[0][0] for st in states)
+            den = sum(np.exp(st[0][0] - m) * st[1][0] for st in states)
+            for (j0, j1), st in zip(parts, states):
+                kw = {"kv_order": kv_order, "S": S, "n_sink": 0}
+                if logits == "device":
+                    a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], **kw)
+                else:
+                    a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], s_device=s_dev[:, j0:j1], **kw)
+                a += a_s[0] * np.exp(st[0][0] - m) * st[1][0] / den
+            if logits == "exact":
+                o_dev = decode_split(s_dev, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
+                a += np.abs(o_dev - o[b, h])
+            allow[b, h] = a
     res = {"o": o}
     if with_allowance:
         res["allow"] = allow

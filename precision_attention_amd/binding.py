@@ -30,6 +30,11 @@ def _declare(lib):
     lib.fp8_attn_fwd_counted.restype = i
     lib.fp8_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i, vp, vp]
     lib.fp8_attn_fwd_ex.restype = i
+    lib.fp8_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fp8_attn_decode_workspace_bytes.restype = ctypes.c_ulonglong
+    lib.fp8_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp, ctypes.c_ulonglong,
+                                    vp]
+    lib.fp8_attn_decode.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -199,6 +204,49 @@ def fwd_ex(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_orde
                              None if counts is None else counts.data_ptr(), _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_fwd_ex")
     return out, counts
+
+
+def decode_default_splits(B: int, Hkv: int, H: int, N: int, target_waves: int = 2048) -> int:
+    """Split count that gives about ``target_waves`` waves (8 per CU on 256 CUs)."""
+    groups = (H // Hkv + 31) // 32
+    units = B * Hkv * groups
+    return max(1, min(N // 64, round(target_waves / units)))
+
+
+def decode(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reverse", S: float = 256.0,
+           n_split: int | None = None, out=None, workspace=None, stream=None):
+    """Split-KV decode: q8 [B,H,d] (one query row per head), k8/v8 [B,Hkv,N,d] E4M3 codes;
+    every query sees all N keys. Returns float32 [B,H,d]. ``workspace`` (optional) is a
+    uint8 device tensor of at least ``fp8_attn_decode_workspace_bytes`` bytes."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    if q8.dim() != 3 or k8.dim() != 4 or tuple(v8.shape) != tuple(k8.shape):
+        raise ValueError("q must be [B, H, d], k and v [B, Hkv, N, d]")
+    B, H, d = q8.shape
+    Bk, Hkv, N, dk = k8.shape
+    if (Bk, dk) != (B, d):
+        raise ValueError(f"k shape {tuple(k8.shape)} does not match q {tuple(q8.shape)}")
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if n_split is None:
+        n_split = decode_default_splits(B, Hkv, H, N)
+    need = lib.fp8_attn_decode_workspace_bytes(B, H, d, int(n_split))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, d] tensor")
+    rc = lib.fp8_attn_decode(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), B, H, Hkv, N, d,
+                             KV_ORDERS[kv_order], float(S), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                             int(n_split), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_decode")
+    return out
 
 
 def kv_block() -> int:

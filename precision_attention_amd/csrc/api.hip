@@ -24,6 +24,7 @@ int check_common(int B, int H, int Hkv, int N, int d, int causal, int kv_order, 
   if (!(S > 0.0f && S <= kE4M3Max)) return FP8ATTN_EINVAL;   // also rejects NaN
   if (d != 64 && d != 128 && d != 256) return FP8ATTN_EUNSUPPORTED;
   if (N % fp8attn::kKvBlock != 0) return FP8ATTN_EUNSUPPORTED;
+  if ((int64_t)N * d > INT32_MAX) return FP8ATTN_EUNSUPPORTED;   // one head's K/V in a buffer range
   const int bm = fp8attn::block_m_for(d);
   const int64_t tiles = (N + bm - 1) / bm;
   if ((int64_t)B * H * tiles > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
@@ -158,6 +159,50 @@ int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool pow2 = is_pow2(S);
   const hipError_t e = counts ? fp8attn::launch_fwd_count(p, d, pow2, s) : fp8attn::launch_fwd(p, d, pow2, s);
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
+unsigned long long fp8_attn_decode_workspace_bytes(int B, int H, int d, int n_split) {
+  if (B <= 0 || H <= 0 || n_split <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
+  return (unsigned long long)B * H * n_split * fp8attn::decode_record_floats(d) * sizeof(float);
+}
+
+int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
+                    int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                    const float* q_descale, const float* k_descale, const float* v_descale,
+                    int n_split, void* workspace, unsigned long long workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale || !workspace) return FP8ATTN_EINVAL;
+  if (kv_order == FP8ATTN_KV_REVERSE_SINK_LAST) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, 0, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (n_split < 1 || n_split > N / fp8attn::kKvBlock) return FP8ATTN_EINVAL;
+  const unsigned long long need = fp8_attn_decode_workspace_bytes(B, H, d, n_split);
+  if (workspace_bytes < need) return FP8ATTN_EINVAL;
+  const int G = H / Hkv;
+  const int n_qgroups = (G + 31) / 32;
+  if ((int64_t)B * Hkv * n_qgroups * n_split > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  if ((int64_t)B * H > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    return FP8ATTN_EUNSUPPORTED;
+  fp8attn::DecodeParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = o;
+  p.ws = static_cast<float*>(workspace);
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.N = N;
+  p.n_split = n_split;
+  p.n_qgroups = n_qgroups;
+  p.reverse = kv_order == FP8ATTN_KV_REVERSE;
+  p.S = S;
+  int e2 = 0;
+  frexpf(S, &e2);
+  p.log2_S = (float)(e2 - 1);
+  p.log2e_rsqrt_d = (float)(1.4426950408889634 / sqrt((double)d));
+  const hipError_t e = fp8attn::launch_decode(p, d, is_pow2(S), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
 }
 

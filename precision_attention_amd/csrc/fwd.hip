@@ -32,39 +32,16 @@
 #include <math.h>
 
 #include "launch.h"
+#include "kernel_common.h"
 
 namespace fp8attn {
 namespace {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, const f32x16& c) {
-  // cbsz/blgp format 0 = E4M3 for both operands; zero scale operands select the
-  // unscaled instruction.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// LDS row swizzle: 16-byte chunk c of row j lives at chunk c ^ swz(j). With
-// swz(j) = (j ^ j>>3) & 7 the 128-bit K-operand reads (16 consecutive rows, one chunk,
-// per cycle) hit distinct bank groups; the transposing V reads and the 128-bit staging
-// writes stay conflict-free as with a plain (j & 7) swizzle (measured with the LDS bank
-// conflict counters).
-template <int SWZ>
-__device__ __forceinline__ int swz_row(int j) { return (j ^ (j >> 3)) & SWZ; }
 
 // Map the linear workgroup id to (b, h, query tile). Workgroups are dispatched to the
 // 8 XCDs round-robin (id % 8); when the kv heads divide evenly, every XCD gets whole kv
 // heads (all their query heads), so K/V of one head stay in one XCD's L2, and within an
 // XCD the tiles run longest-first for causal masking.
-__device__ __forceinline__ void decode_tile(const Params& p, int ntiles, int& b, int& h, int& hk, int& qt) {
+__device__ __forceinline__ void map_tile(const Params& p, int ntiles, int& b, int& h, int& hk, int& qt) {
   const int G = p.H / p.Hkv;
   const int U = p.B * p.Hkv;
   const int total = U * G * ntiles;
@@ -95,25 +72,6 @@ __device__ __forceinline__ void decode_tile(const Params& p, int ntiles, int& b,
 __device__ __forceinline__ unsigned bytes_below(int n) {
   return n >= 4 ? 0x80808080u : (n <= 0 ? 0u : (0x80808080u & ((1u << (8 * n)) - 1u)));
 }
-
-// One LDS-DMA instruction: every lane fetches 16 bytes at base + soff + voff (a raw buffer
-// of `range` bytes, so an offset past it reads zeros) and the wave's 64 x 16 bytes land
-// contiguously at lds_dst (lane L at byte 16 L). Completion is counted by vmcnt.
-__device__ __forceinline__ void lds_dma16(const uint8_t* base, int range, uint8_t* lds_dst,
-                                          int voff, int soff) {
-  constexpr int kRawBufferWord3 = 0x00020000;   // 32-bit data format, untyped access
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, kRawBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
-}
-
-// The waves-per-SIMD floor is device code-generation information only. The host pass
-// leaves it out: given a template-dependent waves_per_eu it emits no launch stub.
-#ifdef __HIP_DEVICE_COMPILE__
-#define FP8ATTN_BOUNDS(threads, waves) __launch_bounds__(threads, waves)
-#else
-#define FP8ATTN_BOUNDS(threads, waves) __launch_bounds__(threads)
-#endif
 
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
 // EXT: the options of fp8_attn_fwd_ex (sink split of block 0, quantized row sum); the
@@ -150,7 +108,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
   const int ntiles = (p.N + kBlockM - 1) / kBlockM;
   int b, h, hk, qt;
-  decode_tile(p, ntiles, b, h, hk, qt);
+  map_tile(p, ntiles, b, h, hk, qt);
 
   const int i0 = qt * kBlockM;
   const int r0 = i0 + wave * kRowsPerWave;

@@ -43,7 +43,28 @@ inline int64_t num_workgroups(const Params& p, int d) {
   return (int64_t)p.B * p.H * tiles;
 }
 
+// Split-KV decode: one query row per (batch, head), all N keys, n_split key ranges.
+struct DecodeParams {
+  const uint8_t* q;                 // [B][H][d] E4M3
+  const uint8_t* k;                 // [B][Hkv][N][d] E4M3
+  const uint8_t* v;                 // [B][Hkv][N][d] E4M3
+  float* o;                         // [B][H][d] fp32
+  float* ws;                        // [B][H][n_split] records of decode_record_floats(d)
+  const float* q_descale;           // [B*H]
+  const float* k_descale;           // [B*Hkv]
+  const float* v_descale;           // [B*Hkv]
+  int B, H, Hkv, N;
+  int n_split;                      // key ranges (1 .. N / 64)
+  int n_qgroups;                    // groups of up to 32 query heads per KV head
+  int reverse;
+  float S, log2_S, log2e_rsqrt_d;
+};
+
+// floats per (row, split) record of the decode workspace: acc[d], m, l, 2 unused (16 B aligned)
+constexpr int decode_record_floats(int d) { return d + 4; }
+
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_fwd_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 

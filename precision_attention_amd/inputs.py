@@ -44,11 +44,19 @@ class Workload:
     v_dist: str = "normal"
     descale: str = "head"
     deltas: tuple = field(default_factory=tuple)
+    decode: bool = False          # one query row per head (the last position), all N keys
 
     def flop(self) -> float:
         """Algorithmic FLOP: 2 GEMMs x 2·d per unmasked (query, key) pair."""
+        if self.decode:
+            return 4.0 * self.d * self.B * self.H * self.N
         pairs = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
         return 4.0 * self.d * self.B * self.H * pairs
+
+    def bytes(self) -> float:
+        """Algorithmic bytes: Q, K, V once (1 B per element) and O once (4 B per element)."""
+        nq = 1 if self.decode else self.N
+        return float(self.B * self.d * (self.H * nq * (1 + 4) + 2 * self.Hkv * self.N))
 
 
 WORKLOADS = {
@@ -66,6 +74,10 @@ WORKLOADS = {
                  orders=("reverse",), scales=(256.0,), v_dist="student_t4", descale="head"),
         Workload("causal_h16_n65536_d256", 1, 16, 16, 65536, 256, True, 12.0,
                  orders=("reverse",), scales=(256.0,), v_dist="student_t4", descale="head"),
+        Workload("decode_gqa_h32_kv8_n131072_d128", 1, 32, 8, 131072, 128, False, 10.0,
+                 orders=("reverse", "forward"), scales=(256.0,), descale="head", decode=True),
+        Workload("decode_b8_gqa_h32_kv8_n32768_d128", 8, 32, 8, 32768, 128, False, 10.0,
+                 orders=("reverse",), scales=(256.0,), descale="head", decode=True),
     ]
 }
 
@@ -100,18 +112,19 @@ def quantize_e4m3(x: np.ndarray, per: str):
 
 def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, *, delta: float, n_sink: int = 4,
                 seed: int = 0, construction: str = "clean", v_dist: str = "normal",
-                descale: str = "head", keep_float: bool = True):
+                descale: str = "head", keep_float: bool = True, n_q: int | None = None):
     """Draw one seeded input set. Random draws: PCG64 ``default_rng(seed)``, Q then K
     then V, each as float32 ``standard_normal`` (V: ``standard_t(4)`` cast to float32).
 
-    Returns a dict with uint8 ``q8`` [B,H,N,d], ``k8``/``v8`` [B,Hkv,N,d], float32
-    descales ``qd`` [B,H], ``kd``/``vd`` [B,Hkv] and, if ``keep_float``, the float32
-    sources ``q``, ``k``, ``v`` (after the sink is planted, before quantization).
+    Returns a dict with uint8 ``q8`` [B,H,n_q,d] (n_q = N unless given: decode draws one
+    query position), ``k8``/``v8`` [B,Hkv,N,d], float32 descales ``qd`` [B,H],
+    ``kd``/``vd`` [B,Hkv] and, if ``keep_float``, the float32 sources ``q``, ``k``, ``v``
+    (after the sink is planted, before quantization).
     """
     if H % Hkv:
         raise ValueError("H must be a multiple of Hkv")
     rng = np.random.default_rng(seed)
-    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    q = rng.standard_normal((B, H, N if n_q is None else n_q, d), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
     if v_dist == "normal":
         v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
@@ -138,9 +151,15 @@ def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, *, delta: float, n_sin
 def make_workload_inputs(w: Workload, *, seed: int = 0, delta: float | None = None,
                          construction: str = "clean", keep_float: bool = True):
     """``make_inputs`` with a workload's sizes and sink/value/descale recipe."""
-    return make_inputs(w.B, w.H, w.Hkv, w.N, w.d, delta=w.delta if delta is None else delta,
-                       n_sink=w.n_sink, seed=seed, construction=construction,
-                       v_dist=w.v_dist, descale=w.descale, keep_float=keep_float)
+    inp = make_inputs(w.B, w.H, w.Hkv, w.N, w.d, delta=w.delta if delta is None else delta,
+                      n_sink=w.n_sink, seed=seed, construction=construction,
+                      v_dist=w.v_dist, descale=w.descale, keep_float=keep_float,
+                      n_q=1 if w.decode else None)
+    if w.decode:                  # q [B, H, d]: the single query position
+        for key in ("q8", "q"):
+            if key in inp:
+                inp[key] = np.ascontiguousarray(inp[key][:, :, 0, :])
+    return inp
 
 
 def sample_rows(N: int, n_rows: int, seed: int = 0, edge: int = 128):

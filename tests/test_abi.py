@@ -115,6 +115,28 @@ def test_sink_last_needs_an_entry_point_with_n_sink(lib):
     assert rc == -1
 
 
+def test_decode_workspace_bytes(lib):
+    assert lib.fp8_attn_decode_workspace_bytes(2, 4, 128, 8) == 2 * 4 * 8 * (128 + 4) * 4
+    assert lib.fp8_attn_decode_workspace_bytes(1, 1, 96, 1) == 0
+    assert lib.fp8_attn_decode_workspace_bytes(0, 1, 64, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(ws=None), -1), (dict(n_split=0), -1),
+    (dict(n_split=3), -1), (dict(ws_bytes=100), -1), (dict(order=2), -1), (dict(S=0.0), -1),
+    (dict(H=3, Hkv=2), -1), (dict(d=80), -2), (dict(N=100), -2), (dict(ws=FAKE + 4), -2),
+    (dict(q=FAKE + 8), -2),
+])
+def test_decode_validation(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=4, Hkv=2, N=128, d=128, order=1, S=256.0,
+             qd=FAKE, kd=FAKE, vd=FAKE, n_split=2, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    rc = lib.fp8_attn_decode(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                             a["order"], a["S"], a["qd"], a["kd"], a["vd"], a["n_split"], a["ws"], a["ws_bytes"],
+                             None)
+    assert rc == status
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

@@ -1,0 +1,88 @@
+"""GPU parity of the split-KV decode (fp8_attn_decode) against the oracle's decode:
+one query row per head (drawn like any query row, so the sink construction applies),
+every query over all N keys, the split partition reproduced by
+the oracle. Same two references as the prefill parity tests: the oracle on the device's
+matrix-core logits with only the rounding-boundary allowance, and on exact logits with
+the matrix-core allowance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from precision_attention_amd import binding
+from precision_attention_amd import inputs as I
+
+from _gpu_util import O_TOL, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_inputs(B, H, Hkv, N, d, delta, seed, descale="head"):
+    inp = I.make_inputs(B, H, Hkv, N, d, delta=delta, seed=seed, descale=descale, keep_float=False, n_q=1)
+    inp["q8"] = np.ascontiguousarray(inp["q8"][:, :, 0, :])        # q [B, H, d]
+    return inp
+
+
+def _check(inp, o_gpu, *, order, S, n_split, label, heads=None):
+    got = o_gpu.cpu().numpy()
+    for logits in ("device", "exact"):
+        ref = A.decode_e4m3(inp["q8"], inp["k8"], inp["v8"], inp["qd"], inp["kd"], inp["vd"], kv_order=order, S=S,
+                            n_split=n_split, logits=logits, with_allowance=True, heads=heads)
+        sel = [(b, h) for b in range(got.shape[0]) for h in range(got.shape[1])] if heads is None else heads
+        idx = tuple(np.array(sel).T)
+        diff = np.abs(got[idx] - ref["o"][idx])
+        excess = diff - (O_TOL + ref["allow"][idx])
+        say(f"  {label} [{logits} logits]: max|dO| {diff.max():.3g}, worst excess {excess.max():.3g}")
+        assert np.isfinite(got).all()
+        assert excess.max() <= 0, f"{label}: exceeds tolerance by {excess.max():.3g}"
+
+
+CASES = [
+    # B, H, Hkv, N, d, order, S, delta, n_split
+    (1, 1, 1, 1024, 64, "reverse", 256.0, 8.0, 1),
+    (1, 1, 1, 1024, 64, "forward", 1.0, 8.0, 4),
+    (1, 1, 1, 1024, 64, "reverse", 448.0, 10.0, 16),           # one block per split
+    (2, 8, 2, 4096, 128, "reverse", 256.0, 10.0, 8),
+    (1, 32, 8, 8192, 128, "forward", 16.0, 12.0, 37),          # uneven split sizes
+    (1, 80, 2, 2048, 64, "reverse", 256.0, 8.0, 5),            # 40 query heads per KV head: two groups
+    (2, 4, 4, 2048, 256, "reverse", 256.0, 10.0, 6),
+    (1, 6, 3, 640, 128, "forward", 3.0, 0.0, 10),              # S not a power of two, no sink
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,order,S,delta,n_split", CASES)
+def test_decode_parity(B, H, Hkv, N, d, order, S, delta, n_split):
+    inp = _decode_inputs(B, H, Hkv, N, d, delta, seed=N + d + n_split)
+    t = to_device(inp)
+    label = f"decode B{B} H{H} Hkv{Hkv} N{N} d{d} {order} S={S} splits={n_split}"
+    say(f"case {label}")
+    o = binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], kv_order=order, S=S, n_split=n_split)
+    torch.cuda.synchronize()
+    _check(inp, o, order=order, S=S, n_split=n_split, label=label)
+
+
+def test_decode_long_context_default_splits():
+    """The measured decode workload's shape (B=1, 32 query heads over 8 KV heads,
+    N = 131072, d = 128) with the default split count; four heads checked in full (the
+    first and last of the first KV head, one in the middle, the last head)."""
+    w = I.WORKLOADS["decode_gqa_h32_kv8_n131072_d128"]
+    inp = I.make_workload_inputs(w, seed=0, keep_float=False)
+    t = to_device(inp)
+    n_split = binding.decode_default_splits(w.B, w.Hkv, w.H, w.N)
+    label = f"{w.name} splits={n_split}"
+    say(f"case {label}")
+    o = binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], kv_order="reverse", S=256.0)
+    torch.cuda.synchronize()
+    _check(inp, o, order="reverse", S=256.0, n_split=n_split, label=label,
+           heads=[(0, 0), (0, 3), (0, 17), (0, 31)])
+
+
+def test_decode_deterministic_and_workspace_reuse():
+    inp = _decode_inputs(1, 8, 2, 4096, 128, 10.0, seed=3)
+    t = to_device(inp)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=t["q8"].device)
+    say("case decode determinism")
+    a = binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], n_split=16, workspace=ws)
+    b = binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], n_split=16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
