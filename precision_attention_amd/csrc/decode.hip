@@ -244,39 +244,88 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 }
 
 // O[b][h][c] = vd * sum_s acc_s[c] 2^(m_s - m) / sum_s l_s 2^(m_s - m), m = max_s m_s.
-// One workgroup per (b, h), one thread per output column.
+// One workgroup of kMergeThreads per (b, h, 64 output columns): all threads find m, then
+// thread t sums column c0 + t % 64 over the splits s = t / 64, t / 64 + P, ... (P = 4),
+// unrolled so that many loads are in flight, and the P partial sums meet in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeCols = 64;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const DecodeParams p) {
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeParams p) {
+  constexpr int REC = decode_record_floats(D);
+  constexpr int P = kMergeThreads / kMergeCols;
+  __shared__ float red[kMergeThreads];
+  __shared__ float part_num[P][kMergeCols];
+  __shared__ float part_den[P];
+  const int bh = blockIdx.x / (D / kMergeCols);
+  const int c0 = (blockIdx.x % (D / kMergeCols)) * kMergeCols;
   const int b = bh / p.H, h = bh - b * p.H;
   const int hk = h / (p.H / p.Hkv);
-  const int cidx = threadIdx.x;
-  constexpr int REC = decode_record_floats(D);
+  const int tid = threadIdx.x;
   const float* ws = p.ws + (size_t)bh * p.n_split * REC;
+
   float m = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) m = fmaxf(m, ws[(size_t)s * REC + D]);
+  for (int s = tid; s < p.n_split; s += kMergeThreads) m = fmaxf(m, ws[(size_t)s * REC + D]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  m = red[0];
+
+  const int cl = tid % kMergeCols, part = tid / kMergeCols;
+  const int c = c0 + cl;
   float num = 0.f, den = 0.f;
-  for (int s = 0; s < p.n_split; ++s) {
+  int s = part;
+  for (; s + 3 * P < p.n_split; s += 4 * P) {
+    float mm[4], aa[4], ll[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* st = ws + (size_t)(s + i * P) * REC;
+      mm[i] = st[D];
+      ll[i] = st[D + 1];
+      aa[i] = st[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float w = fast_exp2(mm[i] - m);
+      num = fmaf(aa[i], w, num);
+      den = fmaf(ll[i], w, den);
+    }
+  }
+  for (; s < p.n_split; s += P) {
     const float* st = ws + (size_t)s * REC;
     const float w = fast_exp2(st[D] - m);
-    num = fmaf(st[cidx], w, num);
+    num = fmaf(st[c], w, num);
     den = fmaf(st[D + 1], w, den);
   }
-  p.o[(size_t)bh * D + cidx] = p.v_descale[b * p.Hkv + hk] * num / den;
+  part_num[part][cl] = num;
+  if (cl == 0) part_den[part] = den;
+  __syncthreads();
+  if (part == 0) {
+    float nt = 0.f, dt = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      nt += part_num[q][cl];
+      dt += part_den[q];
+    }
+    p.o[(size_t)bh * D + c] = p.v_descale[b * p.Hkv + hk] * nt / dt;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int d, bool pow2, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_qgroups * p.n_split)), block(64);
-  const dim3 mgrid((unsigned)(p.B * p.H));
+  const dim3 mgrid((unsigned)(p.B * p.H * (d / kMergeCols)));
 #define FP8ATTN_DECODE(D)                                                                        \
   {                                                                                              \
     if (pow2) hipLaunchKernelGGL((decode_kernel<D, true>), grid, block, 0, stream, p);           \
     else hipLaunchKernelGGL((decode_kernel<D, false>), grid, block, 0, stream, p);               \
     const hipError_t e = hipGetLastError();                                                      \
     if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(D), 0, stream, p);                  \
+    hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(kMergeThreads), 0, stream, p);      \
   }
   switch (d) {
     case 64: FP8ATTN_DECODE(64) break;
