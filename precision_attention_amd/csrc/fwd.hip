@@ -89,8 +89,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
   // staging: one LDS-DMA instruction moves 64 lanes x 16 bytes = 1 KiB of a tile
   constexpr int INST_PER_TILE = TILE / 1024;
-  constexpr int RPW = INST_PER_TILE / kWaves;    // per wave and tile
-  static_assert(INST_PER_TILE % kWaves == 0, "tile must split evenly over the waves");
+  constexpr int RPW = (INST_PER_TILE + kWaves - 1) / kWaves;    // per wave and tile (at most)
   // Double buffers for K and V, four separate arrays so that the compiler can tell a DMA
   // into one buffer from reads of another: K(n), V(n) are read while block n + 1 lands.
   __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
@@ -178,7 +177,8 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   auto dma_tile = [&](const uint8_t* src, int blk, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, goff[r], blk * TILE);
+      if (INST_PER_TILE % kWaves == 0 || wave_s + kWaves * r < INST_PER_TILE)
+        lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, goff[r], blk * TILE);
   };
   // every wave waits for its own DMA, then the barrier publishes all of them
   auto dma_wait_sync = []() __attribute__((always_inline)) {
@@ -281,9 +281,10 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     {
       // the two lane halves trade maxima with v_permlane32_swap (no LDS round trip):
-      // the lower half finds the upper half's value in sw[1], the upper half in sw[0]
+      // swapping a register with itself leaves the lower half's values in every lane of
+      // sw[0] and the upper half's in every lane of sw[1]
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(mx, __uint_as_float(half ? sw[0] : sw[1]));
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
@@ -292,7 +293,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
     // P~ S (exp2 with log2 S folded in for S = 2^k), row sum, E4M3 cast. The first cast
     // of a dword writes its low half and keeps the rest, which the second cast replaces,
-    // so the kept value is arbitrary (no register clearing).
+    // so the kept value is arbitrary.
     int pw[8];   // E4M3 codes of P, four per dword
     float lsum = 0.f;
 #pragma unroll
@@ -304,7 +305,8 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         float x2 = fast_exp2(fmaf(s[t][4 * a + 2], c, bias));
         float x3 = fast_exp2(fmaf(s[t][4 * a + 3], c, bias));
         if (!POW2) { x0 *= p.S; x1 *= p.S; x2 *= p.S; x3 *= p.S; }
-        lsum += (x0 + x1) + (x2 + x3);
+        const float part = (x0 + x1) + (x2 + x3);
+        lsum = (t == 0 && a == 0) ? part : lsum + part;
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_nondeterministic_value(0), false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
         pw[4 * t + a] = w;
