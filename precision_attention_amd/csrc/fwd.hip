@@ -273,27 +273,29 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         }
     }
 
-    // running max: raw maximum, scaled once (c > 0 keeps the order)
+    // running max: raw maximum, scaled once (c > 0 keeps the order). The IEEE maximum
+    // (v_maximum3_f32) needs no quieting of its inputs, unlike fmaxf, and passes NaN on.
     float mx = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, s[t][r]);
     {
       // the two lane halves trade maxima with v_permlane32_swap (no LDS round trip):
       // swapping a register with itself leaves the lower half's values in every lane of
       // sw[0] and the upper half's in every lane of sw[1]
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float m_new = fmaxf(m_run, mx * c);
+    const float m_new = __builtin_elementwise_maximum(m_run, mx * c);
     const float alpha = fast_exp2(m_run - m_new);     // 0 on the first block
     m_run = m_new;
     const float bias = bias_s - m_new;
 
     // P~ S (exp2 with log2 S folded in for S = 2^k), row sum, E4M3 cast. The first cast
     // of a dword writes its low half and keeps the rest, which the second cast replaces,
-    // so the kept value is arbitrary.
+    // so the kept value is arbitrary: it is the previous block's P operand, dead by now,
+    // whose registers the new codes then take over without copies
     int pw[8];   // E4M3 codes of P, four per dword
     float lsum = 0.f;
 #pragma unroll
@@ -307,7 +309,9 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         if (!POW2) { x0 *= p.S; x1 *= p.S; x2 *= p.S; x3 *= p.S; }
         const float part = (x0 + x1) + (x2 + x3);
         lsum = (t == 0 && a == 0) ? part : lsum + part;
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_nondeterministic_value(0), false);
+        // (the option-carrying variant keeps no P across blocks: it has no registers to
+        // spare for it)
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, EXT ? __builtin_nondeterministic_value(0) : pop[4 * t + a], false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
         pw[4 * t + a] = w;
       }
@@ -324,16 +328,16 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     l_run = alpha * l_run + lsum;
 
     if (CNT && !(EXT && part == 2)) {   // the sink keys themselves are never counted
-      // Zero P codes, found four at a time: codes are 0x00..0x7E, so byte + 0x7F never
-      // carries and leaves bit 7 clear exactly for a zero code.
       const int jb = blk * kKvBlock;
       const bool sink_block = jb < p.n_sink;
+      unsigned z;   // zero codes among this lane's counted keys of the block
       if ((p.causal && blk >= diag) || sink_block) {
         // blocks with masked or sink keys: only keys j in [n_sink, hi] count, hi = i for
-        // causal attention.
+        // causal attention. Zero codes are found four at a time: codes are 0x00..0x7E,
+        // so byte + 0x7F never carries and leaves bit 7 clear exactly for a zero code.
         const int hi = p.causal ? i_row : p.N - 1;
         const int n_hi = hi - jb - 4 * half + 1, n_lo = p.n_sink - jb - 4 * half;
-        unsigned z = 0;
+        z = 0;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -343,15 +347,22 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
             const unsigned live = bytes_below(n_hi - k) & ~bytes_below(n_lo - k);
             z += __builtin_popcount(zero & live);
           }
-        cnt_zero += z;
-        if (sink_block) cnt_zero_sink += z;
+        // by value: a conditional update of one of the two counters lets the compiler
+        // merge the updates into a store through a selected address, in scratch
+        cnt_zero_sink += z & (0u - (unsigned)sink_block);
       } else {
-        unsigned nonzero = 0;
+        // every key counts: for a code byte b in [0, 126], |b - 1| + |b - 127| is 126,
+        // plus 2 when b = 0, so two accumulating v_sad_u8 per dword sum to
+        // 8 * 4 * 126 + 2 * (zero codes) over the block's 32 codes of this lane
+        unsigned sad = 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          nonzero += __builtin_popcount(((unsigned)pw[q] + 0x7F7F7F7Fu) & 0x80808080u);
-        cnt_zero += 32u - nonzero;
+        for (int q = 0; q < 8; ++q) {
+          sad = __builtin_amdgcn_sad_u8((unsigned)pw[q], 0x01010101u, sad);
+          sad = __builtin_amdgcn_sad_u8((unsigned)pw[q], 0x7F7F7F7Fu, sad);
+        }
+        z = (sad - 8u * 4u * 126u) >> 1;
       }
+      cnt_zero += z;
     }
     if (OUT) {
       // Rescale only when some row's max moved: alpha == 1 exactly otherwise, and a
@@ -388,7 +399,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     }
   };
 
-  i32x8 pop;   // P of the block, in the B-operand layout of the P.V product
+  i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};   // P of the block, in the B-operand layout of the P.V product
   {
     dma_tile(Kg, block_of(0), kb0);
     if (OUT) dma_tile(Vg, block_of(0), vb0);
