@@ -60,6 +60,28 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def measured_sq(workload: str, achieved_tflops: float):
+    """Clock-adjusted MFMA fraction and the vector-ALU (softmax) co-roofline from the
+    committed SQ-counter record, if it was taken on the current kernel source (else None).
+    The clock is the shader clock the counters saw during the launch; the per-clock MFMA
+    rate is the one the FP8 MFMA stream probe measures."""
+    path = os.path.join(ROOT, "profiles", f"sq_fwd_counted_{workload}.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None, None
+    src = os.path.relpath(path, ROOT)
+    peak = 256 * rec["mfma_flop_per_clk_per_cu"] * rec["sclk_ghz"] * 1e9 / 1e12
+    clock = {"sclk_ghz": rec["sclk_ghz"], "peak": peak, "unit": "TFLOP/s", "frac": achieved_tflops / peak,
+             "source": src}
+    valu = {"bound": "valu", "busy_frac": rec["valu_busy_frac"], "valu_per_wave_step": rec["valu_per_wave_step"],
+            "mfma_per_wave_step": rec["mfma_per_wave_step"], "mfma_busy_frac": rec["mfma_busy_frac"],
+            "coexec_frac_of_mfma": rec["coexec_frac_of_mfma"], "source": src}
+    return clock, valu
+
+
 def quality(inp, w, o_gpu, order, S, n_rows=64, heads=((0, 0), (0, 9), (0, 22), (0, 31))):
     """MSE of the GPU output against exact fp64 attention on the fp32 source tensors, and
     of a bf16 FlashAttention fed the same E4M3 operands (forward order, P rounded to bf16),
@@ -196,6 +218,8 @@ def main():
     wall = time.perf_counter() - wall0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = sum(per) / len(per)
+    ms_median = float(np.median(per))
+    ms_min = min(per)
     flop = w.flop()
     value = flop / (ms_per_step * 1e-3) / 1e12
 
@@ -236,7 +260,11 @@ def main():
                       "causal": w.causal, "kv_order": args.order, "S": args.S, "delta": w.delta,
                       "n_sink": w.n_sink, "descale": w.descale, "sink_construction": "clean", "seed": args.seed},
            "roofline": roofline, "mfma_peak_frac": roofline["frac"], "fwd_only_ms": fwd_only_ms,
-           "fwd_only_tflops": flop / (fwd_only_ms * 1e-3) / 1e12, "wall_s_timed": wall, "collapse": collapse}
+           "fwd_only_tflops": flop / (fwd_only_ms * 1e-3) / 1e12, "wall_s_timed": wall,
+           "step_ms": {"mean": ms_per_step, "median": ms_median, "min": ms_min},
+           "tflops_at_median": flop / (ms_median * 1e-3) / 1e12, "tflops_at_min": flop / (ms_min * 1e-3) / 1e12,
+           "collapse": collapse}
+    out["mfma_peak_frac_clock_adjusted"], out["vector_alu"] = measured_sq(w.name, value)
 
     if not args.no_quality:
         log("bench: quality (MSE vs fp64 on sampled rows, CPU)")

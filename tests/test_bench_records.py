@@ -1,0 +1,77 @@
+"""The measurement records bench.py reads (profiles/*.json): they are reported only while
+they were taken on the current kernel source, and their derived figures follow from the
+raw counter readings they hold."""
+import json
+import os
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+WL = "gqa_causal_h32_kv8_n32768_d128"
+
+
+def _write(tmp_path, name, rec):
+    d = tmp_path / "profiles"
+    d.mkdir(exist_ok=True)
+    (d / name).write_text(json.dumps(rec))
+
+
+def test_records_follow_the_source_hash(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    assert bench.measured_traffic(WL) is None
+    assert bench.measured_sq(WL, 1000.0) == (None, None)
+    sq = {"kernel_source_hash": "abc", "mfma_flop_per_clk_per_cu": 8000, "sclk_ghz": 2.0,
+          "valu_busy_frac": 0.7, "valu_per_wave_step": 190.0, "mfma_per_wave_step": 8.0,
+          "mfma_busy_frac": 0.4, "coexec_frac_of_mfma": 0.6}
+    _write(tmp_path, f"traffic_fwd_counted_{WL}.json", {"kernel_source_hash": "abc", "hbm_bytes_per_launch": 123})
+    _write(tmp_path, f"sq_fwd_counted_{WL}.json", sq)
+    assert bench.measured_traffic(WL) == 123
+    clock, valu = bench.measured_sq(WL, 2048.0)
+    assert clock["peak"] == pytest.approx(256 * 8000 * 2.0e9 / 1e12)
+    assert clock["frac"] == pytest.approx(2048.0 / clock["peak"])
+    assert valu["bound"] == "valu" and valu["busy_frac"] == 0.7
+    # a record of another kernel source is not reported
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "def")
+    assert bench.measured_traffic(WL) is None
+    assert bench.measured_sq(WL, 2048.0) == (None, None)
+
+
+def test_committed_traffic_record_is_consistent():
+    with open(os.path.join(ROOT, "profiles", f"traffic_fwd_counted_{WL}.json")) as f:
+        rec = json.load(f)
+    cal = rec["calibration"]
+    # the factors are what make the copy's counters read its known size
+    assert cal["fetch_factor"] == pytest.approx(cal["copy_bytes"] / 1024 / cal["copy_fetch_size_kib"], rel=1e-3)
+    assert cal["write_factor"] == pytest.approx(cal["copy_bytes"] / 1024 / cal["copy_write_size_kib"], rel=1e-3)
+    hbm = 1024 * (rec["fetch_size_kib_per_launch"] * cal["fetch_factor"]
+                  + rec["write_size_kib_per_launch"] * cal["write_factor"])
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(hbm, rel=1e-6)
+    assert rec["hbm_over_algorithmic"] == pytest.approx(rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"],
+                                                        rel=1e-3)
+    # the write side is O (fp32) at least
+    from precision_attention_amd import inputs as I
+    w = I.WORKLOADS[WL]
+    assert rec["algorithmic_bytes_per_launch"] == w.bytes()
+    assert 1024 * rec["write_size_kib_per_launch"] * cal["write_factor"] >= 4 * w.B * w.H * w.N * w.d
+    for cmd in rec["commands"]:
+        assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
+
+
+def test_committed_sq_record_is_consistent():
+    with open(os.path.join(ROOT, "profiles", f"sq_fwd_counted_{WL}.json")) as f:
+        rec = json.load(f)
+    c = rec["counters_per_launch"]
+    cycles = c["GRBM_GUI_ACTIVE"] / 8
+    assert rec["sclk_ghz"] == pytest.approx(cycles / rec["kernel_median_ns"], rel=1e-3)
+    assert 1.0 < rec["sclk_ghz"] < 2.5
+    assert rec["mfma_per_wave_step"] == pytest.approx(c["SQ_INSTS_MFMA"] / rec["wave_steps_per_launch"], rel=1e-3)
+    assert rec["mfma_busy_frac"] == pytest.approx(c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / cycles, rel=1e-2)
+    # 8 MFMAs per wave-step (4 for S, 4 for P.V at d = 128), 64 cycles each
+    assert rec["mfma_per_wave_step"] == pytest.approx(8.0)
+    assert c["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(64 * c["SQ_INSTS_MFMA"], rel=0.01)
+    assert 0.0 < rec["coexec_frac_of_mfma"] <= 1.0 and 0.0 < rec["valu_busy_frac"] <= 1.0
+    for cmd in rec["commands"]:
+        assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
