@@ -153,6 +153,9 @@ def main():
     ap.add_argument("--order", default="reverse", choices=["reverse", "forward"])
     ap.add_argument("--S", type=float, default=256.0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--construction", default="clean", choices=["clean", "literal"],
+                    help="sink construction of the synthetic inputs (clean: the non-sink keys carry no sink "
+                         "channel; literal: column 0 of those keys stays random)")
     ap.add_argument("--no-quality", action="store_true", help="skip the CPU MSE check")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
@@ -190,7 +193,7 @@ def main():
         return bench_decode(args, w)
     dev = torch.device("cuda:0")
     log(f"bench: generating {w.name} (seed {args.seed})")
-    inp = I.make_workload_inputs(w, seed=args.seed, keep_float=not args.no_quality)
+    inp = I.make_workload_inputs(w, seed=args.seed, construction=args.construction, keep_float=not args.no_quality)
     t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev) for k in ("q8", "k8", "v8", "qd", "kd", "vd")}
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     counts = torch.empty(4, dtype=torch.int64, device=dev)
@@ -258,7 +261,7 @@ def main():
            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                       "causal": w.causal, "kv_order": args.order, "S": args.S, "delta": w.delta,
-                      "n_sink": w.n_sink, "descale": w.descale, "sink_construction": "clean", "seed": args.seed},
+                      "n_sink": w.n_sink, "descale": w.descale, "sink_construction": args.construction, "seed": args.seed},
            "roofline": roofline, "mfma_peak_frac": roofline["frac"], "fwd_only_ms": fwd_only_ms,
            "fwd_only_tflops": flop / (fwd_only_ms * 1e-3) / 1e12, "wall_s_timed": wall,
            "step_ms": {"mean": ms_per_step, "median": ms_median, "min": ms_min},
@@ -286,7 +289,7 @@ def bench_decode(args, w):
 
     dev = torch.device("cuda:0")
     log(f"bench: generating {w.name} (seed {args.seed})")
-    inp = I.make_workload_inputs(w, seed=args.seed, keep_float=False)
+    inp = I.make_workload_inputs(w, seed=args.seed, construction=args.construction, keep_float=False)
     t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev) for k in ("q8", "k8", "v8", "qd", "kd", "vd")}
     n_split = binding.decode_default_splits(w.B, w.Hkv, w.H, w.N)
     o = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
@@ -314,7 +317,8 @@ def bench_decode(args, w):
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                      "kv_order": args.order, "S": args.S, "n_split": n_split, "delta": w.delta},
+                      "kv_order": args.order, "S": args.S, "n_split": n_split, "delta": w.delta,
+                      "sink_construction": args.construction},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
                         "traffic": None, "kernel": "decode_kernel<128,pow2> + decode_merge_kernel",
                         "bytes_per_launch": nbytes},
