@@ -163,22 +163,29 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     }
   }
   auto vaddr = [&](int u, int tw) { return voff[u ^ (tw & (SWZ >> 1))] + 16 * tw * D; };
-  // LDS (row j, 16-byte slot cs) holds global chunk cs ^ swz(j) of row j. Instruction ii of
-  // a tile covers rows (1024 / D) ii .. and lane L lands on LDS bytes 16 L of that KiB, so
-  // it fetches the matching chunk. The offset within the tile is the same for K and V.
+  // LDS (row j, 16-byte slot cs) holds global chunk cs ^ swz(j) of key row j for K, and of
+  // key row j with bits 2 and 3 exchanged for V. Instruction ii of a tile covers LDS rows
+  // (1024 / D) ii .. and lane L lands on LDS bytes 16 L of that KiB, so it fetches the
+  // matching chunk.
+  // The V row order makes the transposed V reads (LDS row 16w + 8h + e for MFMA k-index
+  // 32h + 8w + e) meet P exactly where the E4M3 cast leaves it: lane half h holds, in
+  // byte 16t + 4a + b of its P operand, key 32t + 8a + 4h + b, which is the V row stored
+  // at LDS row 16(2t + a/2) + 8h + 4(a%2) + b. So P needs no exchange between lane halves.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  int goff[RPW];
+  auto swap23 = [](int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); };
+  int goff[RPW], goffv[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int ii = wave + kWaves * r;
     const int j = (1024 / D) * ii + lane / CH, cs = lane % CH;
     goff[r] = j * D + ((cs ^ swz(j)) << 4);
+    goffv[r] = swap23(j) * D + ((cs ^ swz(j)) << 4);
   }
-  auto dma_tile = [&](const uint8_t* src, int blk, uint8_t* dst) __attribute__((always_inline)) {
+  auto dma_tile = [&](const uint8_t* src, int blk, uint8_t* dst, const int (&off)[RPW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (INST_PER_TILE % kWaves == 0 || wave_s + kWaves * r < INST_PER_TILE)
-        lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, goff[r], blk * TILE);
+        lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, off[r], blk * TILE);
   };
   // every wave waits for its own DMA, then the barrier publishes all of them
   auto dma_wait_sync = []() __attribute__((always_inline)) {
@@ -372,15 +379,9 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         for (int u = 0; u < DU; ++u) acc[u] *= alpha;
       }
 
-      // P pairs of 8 consecutive keys: lower half keeps X and takes the upper half's X;
-      // upper half takes the lower half's Y and keeps Y.
-      // v_permlane32_swap(X, Y) swaps X's upper 32 lanes with Y's lower 32 lanes.
+      // the cast codes are the P.V operand as they stand (the V tile's row order matches)
 #pragma unroll
-      for (int tw = 0; tw < 4; ++tw) {
-        const auto r = __builtin_amdgcn_permlane32_swap(pw[2 * tw], pw[2 * tw + 1], false, false);
-        pop[2 * tw] = (int)r[0];
-        pop[2 * tw + 1] = (int)r[1];
-      }
+      for (int q = 0; q < 8; ++q) pop[q] = pw[q];
     }
   };
 
@@ -401,15 +402,15 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
   i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};   // P of the block, in the B-operand layout of the P.V product
   {
-    dma_tile(Kg, block_of(0), kb0);
-    if (OUT) dma_tile(Vg, block_of(0), vb0);
+    dma_tile(Kg, block_of(0), kb0, goff);
+    if (OUT) dma_tile(Vg, block_of(0), vb0, goffv);
     dma_wait_sync();
     // step n on buffers `cur` (a constant 0 or 1 at each call site); block n + 1 lands in
     // the other pair
     auto step = [&](int n, int cur) __attribute__((always_inline)) {
       if (n + 1 < wg_nb) {
-        dma_tile(Kg, block_of(n + 1), kbuf(cur ^ 1));
-        if (OUT) dma_tile(Vg, block_of(n + 1), vbuf(cur ^ 1));
+        dma_tile(Kg, block_of(n + 1), kbuf(cur ^ 1), goff);
+        if (OUT) dma_tile(Vg, block_of(n + 1), vbuf(cur ^ 1), goffv);
       }
       if (active(n)) {
         const int blk = block_of(n);
