@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -39,11 +40,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def strip_comments(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed: what the
+    compiler sees, so that edits to comments do not change the hash. (The kernel sources
+    hold no string or character literals with comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (comments stripped) of the sources the prefill kernel is built from;
+    the measurement records under profiles/ carry the hash of the code they were taken on."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

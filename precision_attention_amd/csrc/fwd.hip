@@ -16,15 +16,16 @@
 //   32-key tile. Row max and row sum are lane-local plus one exchange between the two
 //   lane halves; the running state (m, l) lives in the lane.
 // * P never leaves registers: the 32 fp32 probabilities of a lane are packed to E4M3
-//   four per dword (v_cvt_pk_fp8_f32), then the two lane halves trade one dword per
-//   pair so that every dword pair holds 8 consecutive keys; that pair layout is the B
+//   four per dword (v_cvt_pk_fp8_f32), and those 8 dwords are, as they stand, the B
 //   operand of O^T = V^T . P^T (32 output columns x 32 query rows per MFMA).
-// * V^T comes straight from the row-major V tile in LDS with ds_read_b64_tr_b8: within
-//   each 16-lane group, lane t receives byte t%8 of the 8-byte rows supplied by lanes
-//   2e + t/8 (e = 0..7); supplying 8 consecutive key rows x 16 columns gives each lane
-//   8 consecutive keys of one column, the same key order as the P pairs.
-// * LDS rows are XOR-swizzled at 16-byte granularity (chunk ^ (row % 8)) so that both
-//   the 128-bit K reads and the transposing V reads hit distinct banks.
+// * V^T comes straight from the V tile in LDS with ds_read_b64_tr_b8: within each
+//   16-lane group, lane t receives byte t%8 of the 8-byte rows supplied by lanes
+//   2e + t/8 (e = 0..7), so each lane gets 8 consecutive LDS rows of one column. The V
+//   tile is stored with its key rows' bits 2 and 3 exchanged, which makes those LDS rows
+//   the keys whose P the cast left in the matching bytes of the lane.
+// * LDS rows are XOR-swizzled at 16-byte granularity (chunk ^ ((row ^ row/8) % 8)) so
+//   that the 128-bit K reads, the transposing V reads and the DMA writes hit distinct
+//   banks.
 // * The MFMA operand k-slot order is only required to agree between A and B, so the d
 //   index of Q and K and the key index of P and V may be permuted consistently.
 #include <hip/hip_runtime.h>

@@ -75,3 +75,21 @@ def test_committed_sq_record_is_consistent():
     assert 0.0 < rec["coexec_frac_of_mfma"] <= 1.0 and 0.0 < rec["valu_busy_frac"] <= 1.0
     for cmd in rec["commands"]:
         assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    code = "// header\nint f(int a) { /* note */ return a + 1; }  // tail\n"
+    assert bench.strip_comments(code) == "int f(int a) { return a + 1; }"
+    srcs = []
+    for i, rel in enumerate(bench.KERNEL_SOURCES):
+        path = tmp_path / rel
+        path.parent.mkdir(parents=True, exist_ok=True)
+        path.write_text(f"int x{i} = {i};\n")
+        srcs.append(path)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    srcs[0].write_text("// a comment\nint x0 =   0; /* more */\n")
+    assert bench.kernel_source_hash() == h0
+    srcs[0].write_text("int x0 = 1;\n")
+    assert bench.kernel_source_hash() != h0
+
