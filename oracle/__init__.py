@@ -6,11 +6,15 @@ smoke check and the CPU-baseline leg of the benchmark may import it. The HIP lib
 and its Python binding never import it, and it imports nothing from them.
 
 Modules
-  e4m3       OCP E4M3FN and bf16 codecs (round-to-nearest-even).
-  attention  the block-wise online softmax with the P·S cast, forward or reverse KV
-             order; its closed-form restatement; exact attention; the collapse counter;
-             the rounding-boundary allowance.
-  theory     F(Δ,S), δ_k, Δ_c, d_p(S), the reverse-order bound, fp32 round trips.
+  e4m3        OCP E4M3FN and bf16 codecs (round-to-nearest-even).
+  attention   the block-wise online softmax with the P·S cast, forward or reverse KV
+              order (also the sink-last reverse walk and the quantized row-sum
+              denominator); its closed-form restatement; exact attention; the collapse
+              counter; the rounding-boundary allowance; split-KV decode (split ranges,
+              per-split states, their exact merge).
+  theory      F(Δ,S), δ_k, Δ_c, d_p(S), the reverse-order bound, fp32 round trips.
+  mfma_model  the FP8 matrix core's accumulation, used only to bound which casts the
+              device may round the other way (its arithmetic also in csrc/mfma_model.c).
 
 Pins: every function is checked in tests/test_oracle_*.py against values the pages
 fix, closed forms, textbook routines or brute force. The absolute MSE values of the
