@@ -6,13 +6,15 @@ on sampled rows (first and last 128 rows plus seeded random rows) of a few heads
 collapse counts on properties that hold at any size: exact pair totals, no collapse
 before the sink block for reverse order with S = 256 on the clean sink construction
 (P-Cast technical summary, section 2, Optimization 1), and, for one whole head of the
-causal B4/H32/N8192 workload, the count itself.
+causal B4/H32/N8192 workload, the count itself. On the GQA N = 32768 workload the fused
+launch the benchmark times must reproduce those outputs and counts bit for bit.
 """
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as oracle_attention
+from precision_attention_amd import binding
 from precision_attention_amd import inputs as I
 
 from _gpu_util import check_both, check_counts, gpu_counts, gpu_fwd, pair_counts, say, to_device
@@ -65,9 +67,17 @@ def test_causal_b4_h32_n8192():
 def test_gqa_causal_h32_kv8_n32768(order):
     w = I.WORKLOADS["gqa_causal_h32_kv8_n32768_d128"]
     heads = [(0, 0), (0, 5), (0, 31)] if order == "reverse" else [(0, 2), (0, 19)]
-    _, _, _, c = _run(w, order, 256.0, heads=heads, n_rows=320)
+    _, t, o, c = _run(w, order, 256.0, heads=heads, n_rows=320)
     if order == "reverse":
         assert _presink_fraction_ok(c, w)
+    # the launch the benchmark times (forward and count fused, n_sink = 4) gives exactly
+    # the outputs checked above, over the whole tensors
+    say(f"  fused launch, {order}")
+    of, cf = binding.fwd_counted(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], causal=w.causal,
+                                 kv_order=order, S=256.0, n_sink=w.n_sink)
+    torch.cuda.synchronize()
+    assert torch.equal(of, o)
+    assert list(cf.cpu().numpy().astype(np.int64)) == list(c)
 
 
 @pytest.mark.parametrize("name", ["causal_h16_n65536_d128", "causal_h16_n65536_d256"])
