@@ -34,6 +34,8 @@ PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 matrix peak (no sparsity)
 DEFAULT_WORKLOAD = "gqa_causal_h32_kv8_n32768_d128"
 KERNEL_SOURCES = ["precision_attention_amd/csrc/fwd.hip", "precision_attention_amd/csrc/launch.h",
                   "precision_attention_amd/csrc/kernel_common.h"]
+DECODE_SOURCES = ["precision_attention_amd/csrc/decode.hip", "precision_attention_amd/csrc/launch.h",
+                  "precision_attention_amd/csrc/kernel_common.h"]
 
 
 def log(msg):
@@ -49,25 +51,27 @@ def strip_comments(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the code (comments stripped) of the sources the prefill kernel is built from;
-    the measurement records under profiles/ carry the hash of the code they were taken on."""
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the code (comments stripped) of the sources a kernel is built from (by
+    default the prefill kernel's); the measurement records under profiles/ carry the hash
+    of the code they were taken on."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_fwd_counted_{workload}.json")
+def measured_traffic(workload: str, kind: str = "fwd_counted"):
+    """HBM bytes per launch (per call, for the decode's two kernels) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel code (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    sources = DECODE_SOURCES if kind == "decode" else KERNEL_SOURCES
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -332,7 +336,8 @@ def bench_decode(args, w):
                       "kv_order": args.order, "S": args.S, "n_split": n_split, "delta": w.delta,
                       "sink_construction": args.construction},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
-                        "traffic": None, "kernel": "decode_kernel<128,pow2> + decode_merge_kernel",
+                        "traffic": measured_traffic(w.name, "decode"),
+                        "kernel": "decode_kernel<128,pow2> + decode_merge_kernel",
                         "bytes_per_launch": nbytes},
            "tflops": w.flop() / (ms * 1e-3) / 1e12}
     print(json.dumps(out), flush=True)

@@ -93,3 +93,23 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     srcs[0].write_text("int x0 = 1;\n")
     assert bench.kernel_source_hash() != h0
 
+
+
+@pytest.mark.parametrize("wl", ["decode_gqa_h32_kv8_n131072_d128", "decode_b8_gqa_h32_kv8_n32768_d128"])
+def test_committed_decode_traffic_records_are_consistent(wl):
+    from precision_attention_amd import inputs as I
+
+    with open(os.path.join(ROOT, "profiles", f"traffic_decode_{wl}.json")) as f:
+        rec = json.load(f)
+    cal = rec["calibration"]
+    fetch = 1024 * sum(rec["fetch_size_kib_per_call"].values()) * cal["fetch_factor"]
+    write = 1024 * sum(rec["write_size_kib_per_call"].values()) * cal["write_factor"]
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(fetch + write, rel=1e-6)
+    w = I.WORKLOADS[wl]
+    assert rec["algorithmic_bytes_per_launch"] == w.bytes()
+    # K and V are read at least once; the split records (d + 4 floats per head and split)
+    # and O are written at least once
+    assert fetch >= 2 * w.B * w.Hkv * w.N * w.d
+    assert rec["hbm_over_algorithmic"] == pytest.approx((fetch + write) / w.bytes(), rel=1e-3)
+    for cmd in rec["commands"]:
+        assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
