@@ -20,7 +20,7 @@ def _write(tmp_path, name, rec):
 
 def test_records_follow_the_source_hash(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "abc")
     assert bench.measured_traffic(WL) is None
     assert bench.measured_sq(WL, 1000.0) == (None, None)
     sq = {"kernel_source_hash": "abc", "mfma_flop_per_clk_per_cu": 8000, "sclk_ghz": 2.0,
@@ -34,7 +34,7 @@ def test_records_follow_the_source_hash(tmp_path, monkeypatch):
     assert clock["frac"] == pytest.approx(2048.0 / clock["peak"])
     assert valu["bound"] == "valu" and valu["busy_frac"] == 0.7
     # a record of another kernel source is not reported
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "def")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "def")
     assert bench.measured_traffic(WL) is None
     assert bench.measured_sq(WL, 2048.0) == (None, None)
 
