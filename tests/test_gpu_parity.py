@@ -59,6 +59,38 @@ def test_edge_shapes_full_parity(B, H, Hkv, N, d, causal, order, S, delta):
     assert tuple(c[2:]) == pair_counts(B, H, N, causal)
 
 
+
+def _random_configs(n=12, seed=2024):
+    """Seeded random shapes and options, beyond the hand-picked edge cases: B, H, the
+    grouped-query ratio, N (multiples of 64, not of 128 half the time), d, mask, order,
+    S (powers of two and not) and the sink strength."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.integers(1, 3))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        N = 64 * int(rng.integers(1, 9 if d < 256 else 6))
+        causal = bool(rng.integers(0, 2))
+        order = str(rng.choice(["forward", "reverse"]))
+        S = float(rng.choice([1.0, 2.0, 8.0, 64.0, 256.0, 3.0, 100.0, 448.0]))
+        delta = float(rng.choice([0.0, 4.0, 8.0, 12.0]))
+        out.append((B, H, Hkv, N, d, causal, order, S, delta))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,order,S,delta", _random_configs())
+def test_random_shapes_full_parity(B, H, Hkv, N, d, causal, order, S, delta):
+    inp = I.make_inputs(B, H, Hkv, N, d, delta=delta, seed=7 * N + d + B, descale="head")
+    t = to_device(inp)
+    label = f"random B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} {order} S={S} delta={delta}"
+    say(f"case {label}")
+    o = gpu_fwd(t, causal=causal, order=order, S=S)
+    c = gpu_counts(t, causal=causal, order=order, S=S)
+    check_both(inp, o, c, causal=causal, order=order, S=S, label=label)
+    assert tuple(c[2:]) == pair_counts(B, H, N, causal)
+
 def test_literal_sink_construction():
     inp = I.make_inputs(1, 2, 1, 512, 128, delta=10.0, seed=3, descale="head", construction="literal")
     t = to_device(inp)
