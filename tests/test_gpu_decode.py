@@ -61,6 +61,29 @@ def test_decode_parity(B, H, Hkv, N, d, order, S, delta, n_split):
     _check(inp, o, order=order, S=S, n_split=n_split, label=label)
 
 
+
+def _random_cases(n=10, seed=31):
+    """Seeded random decode shapes: query groups from 1 to 40 heads per KV head, split
+    counts from 1 to every block, both orders, S powers of two and not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.integers(1, 4))
+        H = Hkv * int(rng.choice([1, 4, 8, 40]))
+        N = 64 * int(rng.integers(1, 33 if d < 256 else 17))
+        order = str(rng.choice(["forward", "reverse"]))
+        S = float(rng.choice([1.0, 256.0, 7.0, 448.0]))
+        delta = float(rng.choice([0.0, 8.0, 12.0]))
+        n_split = int(rng.integers(1, N // 64 + 1))
+        out.append((1, H, Hkv, N, d, order, S, delta, n_split))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,order,S,delta,n_split", _random_cases())
+def test_decode_random_parity(B, H, Hkv, N, d, order, S, delta, n_split):
+    test_decode_parity(B, H, Hkv, N, d, order, S, delta, n_split)
+
 def test_decode_long_context_default_splits():
     """The measured decode workload's shape (B=1, 32 query heads over 8 KV heads,
     N = 131072, d = 128) with the default split count; four heads checked in full (the

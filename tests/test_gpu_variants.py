@@ -48,6 +48,31 @@ def test_variant_parity(B, H, Hkv, N, d, causal, order, S, delta, n_sink, denomi
     assert tuple(c[2:]) == pair_counts(B, H, N, causal, n_sink=n_sink)
 
 
+
+def _random_cases(n=10, seed=77):
+    """Seeded random shapes with the fwd_ex options: the three orders, both denominators,
+    n_sink from 0 to 64 (0 to N for the plain orders), S powers of two and not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.integers(1, 3))
+        H = Hkv * int(rng.choice([1, 2]))
+        N = 64 * int(rng.integers(1, 7 if d < 256 else 5))
+        causal = bool(rng.integers(0, 2))
+        order = str(rng.choice(["forward", "reverse", "reverse_sink_last"]))
+        S = float(rng.choice([1.0, 16.0, 256.0, 5.0, 448.0]))
+        delta = float(rng.choice([0.0, 8.0, 12.0]))
+        n_sink = int(rng.choice([0, 1, 4, 17, 64]))
+        denominator = str(rng.choice(["fp32", "quantized"]))
+        out.append((1, H, Hkv, N, d, causal, order, S, delta, n_sink, denominator))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,order,S,delta,n_sink,denominator", _random_cases())
+def test_variant_random_parity(B, H, Hkv, N, d, causal, order, S, delta, n_sink, denominator):
+    test_variant_parity(B, H, Hkv, N, d, causal, order, S, delta, n_sink, denominator)
+
 def test_sink_last_has_no_collapse_on_clean_sinks():
     """What the schedule is for, on the GPU: clean sinks at Δ = 10, S = 256, N = 4096;
     plain reverse collapses part of block 0's non-sink keys, sink-last none at all."""
