@@ -339,12 +339,18 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
       const int jb = blk * kKvBlock;
       const bool sink_block = jb < p.n_sink;
       unsigned z;   // zero codes among this lane's counted keys of the block
-      if ((p.causal && blk >= diag) || sink_block) {
+      // (rare: the diagonal and sink blocks; marked so, the byte masks are not computed
+      // ahead of the branch on every block)
+      if (__builtin_expect((p.causal && blk >= diag) || sink_block, 0)) {
         // blocks with masked or sink keys: only keys j in [n_sink, hi] count, hi = i for
         // causal attention. Zero codes are found four at a time: codes are 0x00..0x7E,
         // so byte + 0x7F never carries and leaves bit 7 clear exactly for a zero code.
         const int hi = p.causal ? i_row : p.N - 1;
-        const int n_hi = hi - jb - 4 * half + 1, n_lo = p.n_sink - jb - 4 * half;
+        int n_hi = hi - jb - 4 * half + 1, n_lo = p.n_sink - jb - 4 * half;
+        // In the option-carrying variant this branch sits in the loop over the parts of a
+        // block; its masks do not depend on the part, and without this opaque (empty)
+        // redefinition the compiler computes them ahead of the branch on every block.
+        if constexpr (EXT) asm volatile("" : "+v"(n_hi), "+v"(n_lo));
         z = 0;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -410,8 +416,12 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
     // the other pair
     auto step = [&](int n, int cur) __attribute__((always_inline)) {
       if (n + 1 < wg_nb) {
-        dma_tile(Kg, block_of(n + 1), kbuf(cur ^ 1), goff);
-        if (OUT) dma_tile(Vg, block_of(n + 1), vbuf(cur ^ 1), goffv);
+        // wave-uniform by construction; said explicitly, since the buffer offset must sit
+        // in a scalar register (the option-carrying variant otherwise wraps each load in a
+        // loop over lanes)
+        const int next = __builtin_amdgcn_readfirstlane(block_of(n + 1));
+        dma_tile(Kg, next, kbuf(cur ^ 1), goff);
+        if (OUT) dma_tile(Vg, next, vbuf(cur ^ 1), goffv);
       }
       if (active(n)) {
         const int blk = block_of(n);
