@@ -30,6 +30,11 @@ def _declare(lib):
     lib.fp8_attn_fwd_counted.restype = i
     lib.fp8_attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i, vp, vp]
     lib.fp8_attn_fwd_ex.restype = i
+    lib.fp8_attn_fwd_exact_qk_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fp8_attn_fwd_exact_qk_workspace_bytes.restype = ctypes.c_ulonglong
+    lib.fp8_attn_fwd_exact_qk.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, i, i, vp, vp,
+                                          ctypes.c_ulonglong, vp]
+    lib.fp8_attn_fwd_exact_qk.restype = i
     lib.fp8_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fp8_attn_decode_workspace_bytes.restype = ctypes.c_ulonglong
     lib.fp8_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp, ctypes.c_ulonglong,
@@ -73,17 +78,39 @@ def _as_codes(t, name):
     return t
 
 
-def _as_descale(t, n, name, device):
+def _check_tensor(t, name, device, dtype, *, shape=None, numel=None, min_bytes=None):
+    """Every tensor whose pointer reaches the library: a torch tensor, contiguous, on
+    ``device`` (the GPU holding q), of ``dtype`` and of the required shape, element count
+    or byte size. Raises ValueError before any library call otherwise."""
     import torch
 
-    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
-        raise ValueError(f"{name}: expected a contiguous float32 device tensor with {n} elements")
-    if t.device != device:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda or t.device != device:
         raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, need at least {min_bytes}")
     return t
 
 
+def _as_descale(t, n, name, device):
+    import torch
+
+    return _check_tensor(t, name, device, torch.float32, numel=n)
+
+
 def _shapes(q8, k8, v8=None):
+    for name, t in (("k", k8), ("v", v8)):
+        if t is not None and t.device != q8.device:
+            raise ValueError(f"{name}: on {t.device}, expected {q8.device} (the device of q)")
     if q8.dim() != 4 or k8.dim() != 4:
         raise ValueError("q and k must be [B, H, N, d] and [B, Hkv, N, d]")
     B, H, N, d = q8.shape
@@ -118,8 +145,7 @@ def fwd(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: 
     vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, N, d))
     rc = lib.fp8_attn_fwd(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                           B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
                           qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), _stream_ptr(dev, stream))
@@ -141,6 +167,7 @@ def p_collapse_count(q8, k8, q_descale, k_descale, *, causal: bool, kv_order: st
     kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
     if out is None:
         out = torch.empty(4, dtype=torch.int64, device=dev)
+    _check_tensor(out, "out", dev, torch.int64, numel=4)
     rc = lib.fp8_attn_p_collapse_count(q8.data_ptr(), k8.data_ptr(), B, H, Hkv, N, d,
                                        int(bool(causal)), KV_ORDERS[kv_order], float(S),
                                        qd.data_ptr(), kd.data_ptr(), int(n_sink), out.data_ptr(),
@@ -164,10 +191,10 @@ def fwd_counted(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv
     vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, N, d))
     if counts is None:
         counts = torch.empty(4, dtype=torch.int64, device=dev)
+    _check_tensor(counts, "counts", dev, torch.int64, numel=4)
     rc = lib.fp8_attn_fwd_counted(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                                   B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
                                   qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink), counts.data_ptr(),
@@ -194,15 +221,52 @@ def fwd_ex(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_orde
     vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, N, d))
     if counts is None and count:
         counts = torch.empty(4, dtype=torch.int64, device=dev)
+    if counts is not None:
+        _check_tensor(counts, "counts", dev, torch.int64, numel=4)
     rc = lib.fp8_attn_fwd_ex(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                              B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
                              qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink), DENOMINATORS[denominator],
                              None if counts is None else counts.data_ptr(), _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_fwd_ex")
+    return out, counts
+
+
+def fwd_exact_qk(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str = "reverse",
+                 S: float = 256.0, n_sink: int = 4, denominator: str = "fp32", count: bool = False,
+                 out=None, counts=None, workspace=None, stream=None):
+    """``fwd_ex`` with Q.K^T from exact products accumulated in fp32 (bf16 matrix cores),
+    d 64 or 128. ``workspace`` (optional): a uint8 device tensor of at least
+    ``fp8_attn_fwd_exact_qk_workspace_bytes`` bytes. Returns (O, counts or None)."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    B, H, Hkv, N, d = _shapes(q8, k8, v8)
+    dev = q8.device
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, N, d))
+    if counts is None and count:
+        counts = torch.empty(4, dtype=torch.int64, device=dev)
+    if counts is not None:
+        _check_tensor(counts, "counts", dev, torch.int64, numel=4)
+    need = int(lib.fp8_attn_fwd_exact_qk_workspace_bytes(B, Hkv, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check_tensor(workspace, "workspace", dev, torch.uint8, min_bytes=need)
+    rc = lib.fp8_attn_fwd_exact_qk(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                   B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                                   qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), int(n_sink),
+                                   DENOMINATORS[denominator], None if counts is None else counts.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_fwd_exact_qk")
     return out, counts
 
 
@@ -233,6 +297,9 @@ def decode(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reve
     if (Bk, dk) != (B, d):
         raise ValueError(f"k shape {tuple(k8.shape)} does not match q {tuple(q8.shape)}")
     dev = q8.device
+    for name, t in (("k", k8), ("v", v8)):
+        if t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, expected {dev} (the device of q)")
     qd = _as_descale(q_descale, B * H, "q_descale", dev)
     kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
     vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
@@ -241,10 +308,10 @@ def decode(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reve
     need = lib.fp8_attn_decode_workspace_bytes(B, H, d, int(n_split))
     if workspace is None:
         workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    _check_tensor(workspace, "workspace", dev, torch.uint8, min_bytes=int(need))
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, d] tensor")
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, d))
     rc = lib.fp8_attn_decode(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), B, H, Hkv, N, d,
                              KV_ORDERS[kv_order], float(S), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
                              int(n_split), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
