@@ -294,74 +294,87 @@ def _e4m3_boundaries():
     return vals, mids
 
 
-def _cast_operand(s, kv_order, S, block, n_sink):
-    m_at_key, m_f = _running_max_at_key(s, kv_order, block, n_sink)
+def _allowance_from(s, v, m_at_key, e_ij, e_run, *, S: float, denominator: str):
+    """The output tolerance of one set of rows, given for every (i, j) the exact running max
+    m_u(j) after the visit that holds key j, a bound e_ij on |device logit - exact logit|,
+    and the bound e_u(j) on the device's running-max error there (the largest e over the
+    keys visited so far: a maximum moves by at most the largest move of its arguments).
+
+    Writing O_i = sum_j c_j e^(m_u(j)) v_j / D_i (c_j the decoded cast code; D_i = S sum_j
+    e^(s_ij) for the fp32 row sum, sum_j c_j e^(m_u(j)) for the quantized one), the device's
+    O' has every s_ij and m_u moved within those bounds and may round P~·S to any code
+    between the codes of the ends of its interval, each end also widened by the relative
+    fp32 band FLIP_REL_WINDOW (the device's own exp2 and scaling). With dc_j the largest
+    move of the code value, g_j = e^(e_u(j)), G_i = e^(max_j e_ij) and w_j = e^(m_u(j) - m_f):
+        dN_ic = sum_j (dc_j g_j + c_j (g_j - 1)) w_j |v_jc|
+        fp32:       |O' - O| <= G (dN / L + |O| (G - 1)),       L = S sum_j e^(s_ij - m_f)
+        quantized:  |O' - O| <= (dN + |O| dD) / (D - dD),       D = sum_j c_j w_j,
+                                                                dD = sum_j (dc_j g_j + c_j (g_j - 1)) w_j
+    (|N' - N| <= dN, D'/D within [1/G, G] or D - dD <= D' <= D + dD). With all e = 0 only the
+    fp32 band remains. Returns (allow [R, d], flagged [R, N]: more than one admissible code,
+    zero_flag [R, N]: admissible codes include zero and a nonzero code, o [R, d])."""
+    va = np.abs(np.asarray(v, dtype=np.float64))
+    vals, _ = _e4m3_boundaries()
     live = np.isfinite(s)
-    with np.errstate(invalid="ignore"):
+    e_ij = np.where(live, e_ij, 0.0)
+    e_run = np.where(live, e_run, 0.0)
+    with np.errstate(invalid="ignore", over="ignore"):
         x = np.where(live, np.exp(s - m_at_key) * S, 0.0)
-    return x, m_at_key, m_f, live
+        m_f = np.where(live, m_at_key, -np.inf).max(axis=1)
+        w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
+    spread = e_ij + e_run
+    code0 = e4m3.encode(x).astype(np.int64) & 0x7F
+    code_lo = e4m3.encode(x * np.exp(-spread) * (1.0 - FLIP_REL_WINDOW)).astype(np.int64) & 0x7F
+    code_hi = e4m3.encode(np.minimum(x * np.exp(spread) * (1.0 + FLIP_REL_WINDOW), S)).astype(np.int64) & 0x7F
+    c0 = np.where(live, vals[code0], 0.0)
+    dc = np.where(live, np.maximum(vals[code_hi] - c0, c0 - vals[code_lo]), 0.0)
+    flagged = live & (code_lo != code_hi)
+    zero_flag = live & (code_lo == 0) & (code_hi != 0)
+    g = np.exp(e_run)
+    G = np.exp(e_ij.max(axis=1))
+    dn_w = (dc * g + c0 * (g - 1.0)) * w
+    dN = dn_w @ va
+    num = (c0 * w) @ np.asarray(v, dtype=np.float64)
+    if denominator == "fp32":
+        with np.errstate(invalid="ignore"):
+            L = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1) * S
+        o = num / L[:, None]
+        allow = G[:, None] * (dN / L[:, None] + np.abs(o) * (G[:, None] - 1.0))
+    elif denominator == "quantized":
+        D = (c0 * w).sum(axis=1)
+        dD = dn_w.sum(axis=1)
+        o = num / D[:, None]
+        with np.errstate(divide="ignore"):
+            allow = np.where((D > dD)[:, None], (dN + np.abs(o) * dD[:, None]) / (D - dD)[:, None], np.inf)
+    else:
+        raise ValueError(denominator)
+    return allow, flagged, zero_flag, o
 
 
-def _codes_near(x, vals, mids):
-    """Nearest code of x and the code across the closest midpoint if x lies within the
-    relative window of that midpoint (else the same code)."""
-    code = e4m3.encode(x).astype(np.int64) & 0x7F
-    lo = np.clip(code - 1, 0, len(mids) - 1)
-    hi = np.clip(code, 0, len(mids) - 1)
-    near_lo = (code > 0) & (np.abs(x - mids[lo]) <= FLIP_REL_WINDOW * mids[lo])
-    near_hi = (code < len(vals) - 1) & (np.abs(x - mids[hi]) <= FLIP_REL_WINDOW * mids[hi])
-    other = np.where(near_lo, code - 1, np.where(near_hi, code + 1, code))
-    return code, other
-
-
-def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_device=None,
+def flip_allowance(s, v, *, kv_order: str, S: float, block: int = BLOCK, s_err=None,
                    n_sink: int = N_SINK_DEFAULT, denominator: str = "fp32"):
-    """Per-element extra tolerance where the device may legitimately pick another E4M3 code.
+    """Per-element tolerance of a device output against the oracle on logits ``s``.
 
-    Two sources are covered. (1) A device evaluating P~·S in fp32 (its own exp) may round
-    a value lying within a relative ``FLIP_REL_WINDOW`` of a rounding midpoint to either
-    neighbour. (2) With ``s_device`` (logits as the device's matrix engine forms them, see
-    ``mfma_model``), the device's P~·S follows those logits and its running max, and may
-    land on a different code than the exact logits give.
-    For every (i, j) the set of admissible codes is: the exact code, the device-logit code,
-    and the neighbour across a midpoint within the window of either value. With dv_ij the
-    largest |admissible - exact code value| and w_ij = exp(m_u - m_f), the allowance of
-    output (i, c) is sum_j dv_ij · w_ij · |v_jc| / L_i; with the quantized denominator the
-    code also enters L_i, which adds sum_j dv_ij · w_ij · |O_ic| / L_i.
+    ``s_err`` (optional, [R, N], natural-log units) bounds how far the device's logits may
+    lie from ``s`` (see ``mfma_model.logit_error_bound``); without it only the device's own
+    fp32 evaluation of P~·S is allowed for: a value within the relative band
+    ``FLIP_REL_WINDOW`` of an E4M3 rounding midpoint may be rounded to either neighbour.
+    With it, every logit and running max may move within its interval, which widens the set
+    of admissible codes and adds the continuous effect on the weights and the row sum (the
+    bound is derived in ``_allowance_from``).
     Returns (allow [R, d], flagged [R, N] bool, zero_flagged [R] int: pairs whose admissible
     codes include both zero and a nonzero code, which can move the collapse count).
     """
     s = np.asarray(s, dtype=np.float64)
-    va = np.abs(np.asarray(v, dtype=np.float64))
-    vals, mids = _e4m3_boundaries()
-    x, m_at_key, m_f, live = _cast_operand(s, kv_order, S, block, n_sink)
-    c0, c1 = _codes_near(x, vals, mids)
-    cands = [c0, c1]
-    if s_device is not None:
-        xd, _, _, _ = _cast_operand(np.asarray(s_device, dtype=np.float64), kv_order, S, block, n_sink)
-        d0, d1 = _codes_near(xd, vals, mids)
-        cands += [d0, d1]
-    dev = np.zeros_like(x)
-    has_zero = np.zeros(x.shape, dtype=bool)
-    has_nonzero = np.zeros(x.shape, dtype=bool)
-    for c in cands:
-        dev = np.maximum(dev, np.abs(vals[c] - vals[c0]))
-        has_zero |= c == 0
-        has_nonzero |= c != 0
-    flagged = live & (dev > 0)
-    zero_flag = live & has_zero & has_nonzero
-    with np.errstate(invalid="ignore"):
-        w = np.where(live, np.exp(m_at_key - m_f[:, None]), 0.0)
-        if denominator == "fp32":
-            L = np.where(live, np.exp(s - m_f[:, None]), 0.0).sum(axis=1) * S
-        else:
-            L = (np.where(live, vals[c0], 0.0) * w).sum(axis=1)
-    weight = np.where(flagged, dev * w, 0.0) / L[:, None]
-    allow = weight @ va
-    if denominator == "quantized":
-        o = online_softmax_pcast_vectorized(s, v, kv_order=kv_order, S=S, block=block, n_sink=n_sink,
-                                            denominator="quantized")
-        allow = allow + weight.sum(axis=1, keepdims=True) * np.abs(o)
+    m_at_key, _ = _running_max_at_key(s, kv_order, block, n_sink)
+    if s_err is None:
+        e_ij = np.zeros_like(s)
+        e_run = e_ij
+    else:
+        e_ij = np.where(np.isfinite(s), np.asarray(s_err, dtype=np.float64), 0.0)
+        e_run, _ = _running_max_at_key(np.where(np.isfinite(s), e_ij, -np.inf), kv_order, block, n_sink)
+        e_run = np.where(np.isfinite(e_run), e_run, 0.0)
+    allow, flagged, zero_flag, _ = _allowance_from(s, v, m_at_key, e_ij, e_run, S=S, denominator=denominator)
     return allow, flagged, zero_flag.sum(axis=1)
 
 
@@ -416,13 +429,25 @@ def decode_split(s, v, *, kv_order: str, S: float, n_split: int, p_cast: str = "
     return num / den[:, None]
 
 
+def _split_running_max(s, kv_order: str, n_split: int, block: int = BLOCK):
+    """Per key, the running max of its own split right after visiting its block (each split
+    walks its blocks in ``kv_order`` from -inf), as ``_running_max_at_key`` for one split."""
+    out = np.full(s.shape, -np.inf)
+    for (j0, j1) in split_ranges(s.shape[1], n_split, block):
+        out[:, j0:j1], _ = _running_max_at_key(s[:, j0:j1], kv_order, block, 0)
+    return out
+
+
 def decode_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str, S: float, n_split: int,
-                logits: str = "exact", with_allowance: bool = False, heads=None):
+                logits: str = "exact", with_allowance: bool = False, heads=None,
+                qk_accumulation: str = "e4m3_mfma"):
     """Decode oracle over E4M3 inputs: q8 [B, H, d] (one query row per head), k8/v8
     [B, Hkv, N, d]; every query sees all N keys. ``heads``: optional list of (b, h) to
-    compute (the others stay 0). Returns dict with ``o`` [B, H, d] and, if asked, ``allow``
-    (the rounding-boundary allowance of ``flip_allowance`` evaluated on each split, plus
-    |O(device logits) - O(exact logits)| for exact logits)."""
+    compute (the others stay 0). Returns dict with ``o`` [B, H, d] and, if asked, ``allow``:
+    for exact logits, the tolerance of ``_allowance_from`` with the logit interval of
+    ``mfma_model.logit_error_bound`` (``qk_accumulation``) and the split-local running maxima
+    (the merged output is sum_j c_j e^(m_u(j)) v_j / (S sum_j e^(s_j)) with m_u(j) the running
+    max of key j's own split, so the same bound holds); for device logits, the fp32 band only."""
     B, H, d = q8.shape
     Hkv = k8.shape[1]
     group = H // Hkv
@@ -433,32 +458,25 @@ def decode_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str, S
     for b, h in heads:
         hk = h // group
         qrow = q8[b, h][None, :]
-        s_exact, _ = head_logits_e4m3(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
-        s_dev = None
-        if logits == "device" or with_allowance:
-            s_dev = mfma_model.model_logits(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
-        s = s_exact if logits == "exact" else s_dev
+        if logits == "exact":
+            s, _ = head_logits_e4m3(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+        elif logits == "device":
+            s = mfma_model.model_logits(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d)
+        else:
+            raise ValueError(logits)
         vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
         o[b, h] = decode_split(s, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
         if with_allowance:
-            a = np.zeros(d)
-            parts = split_ranges(s.shape[1], n_split)
-            # each split's own allowance, weighted by the share of the merged row sum it holds
-            states = [online_softmax_state(s[:, j0:j1], vf[j0:j1], kv_order=kv_order, S=S)
-                      for (j0, j1) in parts]
-            m = max(st[0][0] for st in states)
-            den = sum(np.exp(st[0][0] - m) * st[1][0] for st in states)
-            for (j0, j1), st in zip(parts, states):
-                kw = {"kv_order": kv_order, "S": S, "n_sink": 0}
-                if logits == "device":
-                    a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], **kw)
-                else:
-                    a_s, _, _ = flip_allowance(s[:, j0:j1], vf[j0:j1], s_device=s_dev[:, j0:j1], **kw)
-                a += a_s[0] * np.exp(st[0][0] - m) * st[1][0] / den
+            m_at_key = _split_running_max(s, kv_order, n_split)
             if logits == "exact":
-                o_dev = decode_split(s_dev, vf, kv_order=kv_order, S=S, n_split=n_split)[0]
-                a += np.abs(o_dev - o[b, h])
-            allow[b, h] = a
+                e_ij = mfma_model.logit_error_bound(qrow, k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                                    accumulation=qk_accumulation)
+                e_run = _split_running_max(e_ij, kv_order, n_split)
+            else:
+                e_ij = np.zeros_like(s)
+                e_run = e_ij
+            a, _, _, _ = _allowance_from(s, vf, m_at_key, e_ij, e_run, S=S, denominator="fp32")
+            allow[b, h] = a[0]
     res = {"o": o}
     if with_allowance:
         res["allow"] = allow
@@ -471,19 +489,21 @@ def decode_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str, S
 
 def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, kv_order: str,
                    S: float, rows=None, heads=None, n_sink: int = N_SINK_DEFAULT, logits: str = "exact",
-                   with_allowance: bool = False, with_counts: bool = False, denominator: str = "fp32"):
+                   with_allowance: bool = False, with_counts: bool = False, denominator: str = "fp32",
+                   qk_accumulation: str = "e4m3_mfma"):
     """Oracle over [B, H, N, d] E4M3 inputs (GQA: query head h reads kv head h // (H/Hkv)).
 
     ``q_descale`` is [B, H], ``k_descale``/``v_descale`` are [B, Hkv]. ``rows`` limits the
     query rows (same subset for every head); ``heads`` is an optional list of (b, h).
 
-    ``logits``: "exact" (the exact dot products of the decoded codes) or "device" (the
-    dot products as the gfx950 FP8 matrix core forms them, ``mfma_model``); the rest of
-    the algorithm is identical. ``with_allowance`` adds a per-element tolerance:
-      * for "device": only the fp32 rounding-boundary band around its own P~·S;
-      * for "exact": the codes the device may reach through its matrix-core logits (and the
-        band around both), plus |O(device logits) - O(exact logits)|, the continuous effect
-        of those logits on the row sum and rescaling.
+    ``logits``: "exact" (the exact dot products of the decoded codes: the pages' result) or
+    "device" (the dot products as the gfx950 FP8 matrix core forms them, ``mfma_model``: a
+    secondary reference); the rest of the algorithm is identical. ``with_allowance`` adds a
+    per-element tolerance (``flip_allowance``):
+      * for "exact": the logit interval of ``mfma_model.logit_error_bound`` for the device's
+        Q·K^T accumulation ``qk_accumulation`` ("e4m3_mfma": the FP8 matrix core; "fp32": a
+        matrix core with exact products and fp32 accumulation), with the fp32 band;
+      * for "device": only the fp32 band around its own P~·S.
     Returns dict with ``o`` [len(heads), R, d], ``rows``, ``heads`` and, if asked,
     ``allow`` (same shape as o), ``zero_flagged`` and ``counts`` (summed over heads).
     ``n_sink`` sets the sink tokens of the counts and of "reverse_sink_last";
@@ -501,24 +521,23 @@ def attention_e4m3(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool,
     idx = None
     for (b, h) in heads:
         hk = h // group
-        s_exact, idx = head_logits_e4m3(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+        if logits == "exact":
+            s, idx = head_logits_e4m3(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                      rows=rows, causal=causal)
+        else:
+            s = mfma_model.model_logits(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
                                         rows=rows, causal=causal)
-        s_dev = None
-        if logits == "device" or with_allowance:
-            s_dev = mfma_model.model_logits(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
-                                            rows=rows, causal=causal)
-        s = s_exact if logits == "exact" else s_dev
+            idx = np.arange(N) if rows is None else np.asarray(rows)
         vf = e4m3.decode(v8[b, hk]) * float(v_descale[b, hk])
         opts = {"kv_order": kv_order, "S": S, "n_sink": n_sink, "denominator": denominator}
         o, _ = online_softmax_pcast(s, vf, **opts)
         outs.append(o)
         if with_allowance:
-            if logits == "device":
-                a, _, z = flip_allowance(s_dev, vf, **opts)
-            else:
-                a, _, z = flip_allowance(s_exact, vf, s_device=s_dev, **opts)
-                o_dev, _ = online_softmax_pcast(s_dev, vf, **opts)
-                a = a + np.abs(o_dev - o)
+            s_err = None
+            if logits == "exact":
+                s_err = mfma_model.logit_error_bound(q8[b, h], k8[b, hk], q_descale[b, h], k_descale[b, hk], d,
+                                                     rows=rows, accumulation=qk_accumulation)
+            a, _, z = flip_allowance(s, vf, s_err=s_err, **opts)
             allows.append(a)
             zflag += int(z.sum())
         if with_counts:

@@ -8,8 +8,15 @@ import torch
 from oracle import attention as oracle_attention
 from precision_attention_amd import binding
 
-O_TOL = 2e-3          # max-abs on unit-scale O (plus the rounding-boundary allowance)
+O_TOL = 2e-3          # max-abs on unit-scale O (plus the allowance of the reference)
 COUNT_REL_TOL = 0.005  # collapse count: 0.5% relative (or the boundary-flagged pairs)
+# Against the exact-logit oracle (the pages' result), beside the element-wise tolerance:
+# the fraction of checked rows whose deviation exceeds O_TOL anywhere, and the largest
+# deviation. Both stem from the logit error of Q.K^T and from P·S values next to an E4M3
+# rounding midpoint (a sink's code moving one E4M3 step, at most 1/8 of its value, moves
+# its row by up to ~0.25 with heavy-tailed V).
+ROWS_BEYOND_LIMIT = {"e4m3_mfma": 0.05, "fp32": 0.01}
+MAX_DEV_LIMIT = 0.5
 
 
 def say(msg):
@@ -41,24 +48,30 @@ def gpu_counts(t, *, causal, order, S, n_sink=4):
     return c.cpu().numpy().astype(np.int64)
 
 
-def oracle(inp, *, causal, order, S, rows=None, heads=None, counts=False, n_sink=4, logits="device",
-           denominator="fp32"):
+def oracle(inp, *, causal, order, S, rows=None, heads=None, counts=False, n_sink=4, logits="exact",
+           denominator="fp32", qk="e4m3_mfma"):
     return oracle_attention.attention_e4m3(inp["q8"], inp["k8"], inp["v8"], inp["qd"], inp["kd"], inp["vd"],
                                            causal=causal, kv_order=order, S=S, rows=rows, heads=heads,
                                            n_sink=n_sink, logits=logits, with_allowance=True,
-                                           with_counts=counts, denominator=denominator)
+                                           with_counts=counts, denominator=denominator, qk_accumulation=qk)
 
 
-def check_output(o_gpu, ref, label=""):
-    """o_gpu: full [B,H,N,d] device tensor; ref: oracle dict (heads x rows)."""
+def check_output(o_gpu, ref, label="", qk=None):
+    """o_gpu: full [B,H,N,d] device tensor; ref: oracle dict (heads x rows). Every element
+    within O_TOL plus its allowance; with ``qk`` (an exact-logit reference) also the row
+    fraction beyond O_TOL and the largest deviation within their limits."""
     got = np.stack([o_gpu[b, h].cpu().numpy()[ref["rows"]] for (b, h) in ref["heads"]])
     diff = np.abs(got - ref["o"])
     excess = diff - (O_TOL + ref["allow"])
-    rows_allow = int(((diff > O_TOL).any(axis=2)).sum())
-    say(f"  {label}: max|dO| {diff.max():.3g}  rows beyond {O_TOL} (inside their allowance) {rows_allow}"
-        f" of {diff.shape[0] * diff.shape[1]}")
+    beyond = (diff > O_TOL).any(axis=2)
+    n_rows = diff.shape[0] * diff.shape[1]
+    say(f"  {label}: max|dO| {diff.max():.3g}; rows beyond {O_TOL}: {int(beyond.sum())} of {n_rows} "
+        f"({beyond.mean():.4f}); worst excess over tolerance {excess.max():.3g}")
     assert np.isfinite(got).all(), "non-finite output"
     assert excess.max() <= 0, f"{label}: output exceeds tolerance by {excess.max():.3g}"
+    if qk is not None:
+        assert beyond.mean() <= ROWS_BEYOND_LIMIT[qk], f"{label}: {beyond.mean():.4f} of rows beyond {O_TOL}"
+        assert diff.max() <= MAX_DEV_LIMIT, f"{label}: max|dO| {diff.max():.3g}"
     return diff.max()
 
 
@@ -71,14 +84,19 @@ def check_counts(c_gpu, c_ref, zero_flagged, label=""):
 
 
 def check_both(inp, o, c, *, causal, order, S, label, rows=None, heads=None, count_heads=None, n_sink=4,
-               denominator="fp32"):
-    """Tight check against the oracle on the device's matrix-core logits, then the check
-    against the exact-logit oracle with its wider (matrix-core aware) tolerance."""
-    opts = {"n_sink": n_sink, "denominator": denominator}
-    for logits in ("device", "exact"):
+               denominator="fp32", qk="e4m3_mfma"):
+    """The check against the pages' result first: the exact-logit oracle, with the
+    tolerance that the logit interval of the device's Q.K^T accumulation ``qk`` implies
+    (analytic, from the stated accumulation rule) and limits on the rows beyond O_TOL.
+    Then, for the FP8 matrix-core path, the secondary check against the oracle run on the
+    matrix core's own logits with only the fp32 band as allowance (softmax, cast and
+    block order checked without the logit error)."""
+    opts = {"n_sink": n_sink, "denominator": denominator, "qk": qk}
+    refs = [("exact", True)] + ([("device", False)] if qk == "e4m3_mfma" else [])
+    for logits, primary in refs:
         ref = oracle(inp, causal=causal, order=order, S=S, rows=rows, heads=heads, logits=logits,
                      counts=c is not None and count_heads is None, **opts)
-        check_output(o, ref, f"{label} [{logits} logits]")
+        check_output(o, ref, f"{label} [{logits} logits]", qk=qk if primary else None)
         if c is not None:
             cref = ref if count_heads is None else oracle(inp, causal=causal, order=order, S=S, heads=count_heads,
                                                           logits=logits, counts=True, **opts)

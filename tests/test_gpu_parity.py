@@ -1,12 +1,15 @@
 """GPU parity at sizes the oracle finishes in seconds: the HIP forward and collapse
 count, called through the C ABI, against the fp64 oracle element by element.
 
-Two references per case. (1) The oracle run on the logits the gfx950 FP8 matrix core
-forms (oracle.mfma_model): |O_gpu - O_oracle| <= 2e-3 plus an allowance only where P·S
-sits within 2^-16 (relative) of an E4M3 rounding midpoint. (2) The oracle on exact
-logits, whose allowance adds the codes the matrix core's accumulation can move and its
-continuous effect on the row sum. Pair counts exact; collapse counts within 0.5% (or the
-boundary-flagged pairs).
+Two references per case. (1) The pages' result: the oracle on the exact logits of the
+decoded codes. The tolerance is 2e-3 plus an allowance derived from a bound on the FP8
+matrix core's Q.K^T error (the stated truncation rule, evaluated as an interval per
+query-key pair: never from running the model) and the fp32 band around E4M3 rounding
+midpoints; the fraction of rows beyond 2e-3 and the largest deviation are printed and
+held below fixed limits. (2) A secondary check: the oracle run on the logits the matrix
+core forms (oracle.mfma_model), with only the fp32 band as allowance, which checks the
+softmax, the cast and the block order without the logit error. Pair counts exact;
+collapse counts within 0.5% (or the boundary-flagged pairs).
 """
 import numpy as np
 import pytest

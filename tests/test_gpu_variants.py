@@ -1,8 +1,9 @@
 """GPU parity of the two options of fp8_attn_fwd_ex against the oracle: the sink-last
 reverse schedule (block 0's non-sink keys visited before the sink tokens) and the
 quantized row-sum denominator. Same two-reference check as the main parity tests
-(device-logit oracle tight, exact-logit oracle with the matrix-core allowance); pair
-counts exact, collapse counts within 0.5% or the boundary-flagged pairs."""
+(exact-logit oracle with the analytic logit-interval allowance, then the device-logit
+oracle with the fp32 band only); pair counts exact, collapse counts within 0.5% or the
+boundary-flagged pairs."""
 import numpy as np
 import pytest
 import torch
