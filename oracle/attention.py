@@ -284,6 +284,32 @@ def collapse_counts(s, *, kv_order: str, S: float, n_sink: int = N_SINK_DEFAULT,
     return out
 
 
+def collapse_count_slack(s, *, kv_order: str, S: float, s_err=None, n_sink: int = N_SINK_DEFAULT,
+                         block: int = BLOCK):
+    """How far a device's collapse count may legitimately differ from ``collapse_counts``:
+    the counted (unmasked, non-sink) pairs whose cast operand could land on either side of
+    the zero boundary 2^-10 (E4M3 rounds x <= 2^-10 to zero), given the relative fp32 band
+    FLIP_REL_WINDOW around P~·S and, with ``s_err``, the logit interval of the device's Q·K^T
+    (the same interval as ``flip_allowance``). Returns [all blocks, blocks holding a sink]."""
+    s = np.asarray(s, dtype=np.float64)
+    live = np.isfinite(s)
+    m_at_key, _ = _running_max_at_key(s, kv_order, block, n_sink)
+    if s_err is None:
+        spread = np.zeros_like(s)
+    else:
+        e_ij = np.where(live, np.asarray(s_err, dtype=np.float64), 0.0)
+        e_run, _ = _running_max_at_key(np.where(live, e_ij, -np.inf), kv_order, block, n_sink)
+        spread = e_ij + np.where(np.isfinite(e_run), e_run, 0.0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = np.where(live, np.exp(s - m_at_key) * S, 0.0)
+    zero = 2.0 ** -10
+    both = (x * np.exp(-spread) * (1.0 - FLIP_REL_WINDOW) <= zero) & (x * np.exp(spread) * (1.0 + FLIP_REL_WINDOW) > zero)
+    keys = np.arange(s.shape[1])
+    counted = live & (keys >= n_sink)[None, :] & both
+    sink_cols = keys < ((n_sink + block - 1) // block) * block
+    return np.array([int(counted.sum()), int(counted[:, sink_cols].sum())], dtype=np.int64)
+
+
 # --------------------------------------------------------------------------------------
 # rounding-boundary allowance
 # --------------------------------------------------------------------------------------
@@ -325,7 +351,9 @@ def _allowance_from(s, v, m_at_key, e_ij, e_run, *, S: float, denominator: str):
     spread = e_ij + e_run
     code0 = e4m3.encode(x).astype(np.int64) & 0x7F
     code_lo = e4m3.encode(x * np.exp(-spread) * (1.0 - FLIP_REL_WINDOW)).astype(np.int64) & 0x7F
-    code_hi = e4m3.encode(np.minimum(x * np.exp(spread) * (1.0 + FLIP_REL_WINDOW), S)).astype(np.int64) & 0x7F
+    # no clip at S: a device's own maximum may come out of its exp2 a rounding above 1
+    # (it subtracts a separately rounded product), which matters when S sits on a midpoint
+    code_hi = e4m3.encode(np.minimum(x * np.exp(spread) * (1.0 + FLIP_REL_WINDOW), 448.0)).astype(np.int64) & 0x7F
     c0 = np.where(live, vals[code0], 0.0)
     dc = np.where(live, np.maximum(vals[code_hi] - c0, c0 - vals[code_lo]), 0.0)
     flagged = live & (code_lo != code_hi)

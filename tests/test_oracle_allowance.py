@@ -140,3 +140,65 @@ def test_allowance_without_interval_is_the_band():
     v[1] = [1.0, -1.0]
     allow, flagged, zf = A.flip_allowance(s, v, kv_order="forward", S=1.0)
     assert not flagged.any() and zf[0] == 0 and (allow == 0).all()
+
+
+def test_allowance_covers_a_maximum_on_a_midpoint():
+    """S = 100 puts the row maximum's P~·S = 100 exactly on the E4M3 midpoint between 96
+    and 104; a device whose exp2 returns the maximum a rounding above 1 rounds it up. Both
+    codes must be admissible (found on the GPU: a clip of the interval at S missed it)."""
+    s = np.full((1, 64), -np.inf)
+    s[0, 0] = 0.0
+    s[0, 1] = -1.0
+    v = np.zeros((64, 1))
+    v[0, 0] = 1.0
+    v[1, 0] = -1.0
+    allow, flagged, _ = A.flip_allowance(s, v, kv_order="forward", S=100.0)
+    L = 100.0 * (1.0 + math.exp(-1.0))
+    assert flagged[0, 0]
+    assert allow[0, 0] >= 8.0 / L * 0.999
+
+
+def test_count_slack_agrees_with_the_allowance_zero_flags():
+    """The cheap count slack and the full allowance's zero flags describe the same pairs."""
+    inp = I.make_inputs(1, 1, 1, 512, 64, delta=10.0, seed=9, descale="head", keep_float=False)
+    s, _ = A.head_logits_e4m3(inp["q8"][0, 0], inp["k8"][0, 0], inp["qd"][0, 0], inp["kd"][0, 0], 64)
+    err = mfma_model.logit_error_bound(inp["q8"][0, 0], inp["k8"][0, 0], inp["qd"][0, 0], inp["kd"][0, 0], 64)
+    for order, S in (("forward", 256.0), ("reverse", 16.0), ("forward", 1.0)):
+        _, _, zf = A.flip_allowance(s, np.zeros((512, 1)), kv_order=order, S=S, s_err=err, n_sink=0)
+        slack = A.collapse_count_slack(s, kv_order=order, S=S, s_err=err, n_sink=0)
+        assert slack[0] == int(zf.sum()) and slack[0] > 0
+
+
+def test_decode_allowance_sound_by_brute_force():
+    """The split-KV decode's tolerance (split-local running maxima) holds every output the
+    logit interval can produce, with the merge rerun on moved logits."""
+    rng = np.random.default_rng(4)
+    inp = I.make_inputs(1, 2, 1, 1024, 64, delta=10.0, seed=12, descale="head", keep_float=False, n_q=1)
+    q8 = np.ascontiguousarray(inp["q8"][:, :, 0, :])
+    for order, n_split, S in (("reverse", 4, 256.0), ("forward", 7, 1.0)):
+        res = A.decode_e4m3(q8, inp["k8"], inp["v8"], inp["qd"], inp["kd"], inp["vd"], kv_order=order, S=S,
+                            n_split=n_split, with_allowance=True)
+        for h in range(2):
+            s, _ = A.head_logits_e4m3(q8[0, h][None], inp["k8"][0, 0], inp["qd"][0, h], inp["kd"][0, 0], 64)
+            err = mfma_model.logit_error_bound(q8[0, h][None], inp["k8"][0, 0], inp["qd"][0, h], inp["kd"][0, 0], 64)
+            vf = e4m3.decode(inp["v8"][0, 0]) * float(inp["vd"][0, 0])
+            worst = 0.0
+            for sg in [np.ones_like(s), -np.ones_like(s)] + [rng.uniform(-1, 1, s.shape) for _ in range(30)]:
+                o = A.decode_split(s + sg * err, vf, kv_order=order, S=S, n_split=n_split)[0]
+                worst = max(worst, float((np.abs(o - res["o"][0, h]) / res["allow"][0, h]).max()))
+            assert worst <= 1.0 + 1e-9, worst
+
+
+def test_float_logits_closed_forms():
+    """head_logits_float: orthogonal rows give zero logits off the diagonal and |q|^2/sqrt(d)
+    on it; scaling q by a scales every logit by a; causal masking hides j > i only."""
+    d = 8
+    q = np.eye(d) * np.arange(1, d + 1)[:, None]
+    s, idx = A.head_logits_float(q, q, d)
+    assert np.array_equal(idx, np.arange(d))
+    assert np.allclose(s, np.diag(np.arange(1, d + 1) ** 2 / math.sqrt(d)), rtol=0, atol=1e-15)
+    s3, _ = A.head_logits_float(3.0 * q, q, d)
+    assert np.allclose(s3, 3.0 * s, rtol=1e-15, atol=0)
+    sc, _ = A.head_logits_float(q, q, d, causal=True, rows=[2, 5])
+    assert np.isneginf(sc[0, 3:]).all() and np.isfinite(sc[0, :3]).all()
+    assert np.isneginf(sc[1, 6:]).all() and np.isfinite(sc[1, :6]).all()

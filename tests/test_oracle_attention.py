@@ -264,15 +264,33 @@ def test_mse_ratios_match_printed_ranges():
     assert abs(mse[("reverse", 256.0)] / mse[("forward", 256.0)] - 1.0) < 0.02
 
 
-@pytest.mark.parametrize("delta", [7.0, 8.0, 10.0])
-def test_s256_beats_s448_forward(delta):
-    """Printed: forward S=256 has lower MSE than forward S=448 (d_p is 14% larger at 448).
-    The printed size of the gain (10-15%) belongs to the pages' own P distribution, which
-    they do not give; on this synthetic recipe the gain is a few percent. The direction is
-    pinned, the size is reported."""
+@pytest.mark.parametrize("delta,lo,hi", [(7.0, 0.02, 0.05), (8.0, 0.03, 0.06), (10.0, 0.04, 0.07)])
+def test_s256_beats_s448_forward(delta, lo, hi):
+    """Printed: forward S=256 has lower MSE than forward S=448 (d_p is 14% larger at 448),
+    by 10-15% on the pages' own, unstated, P distribution. On this recipe (Q, K, V fp32, the
+    sinks' logit noise shared through Q·K^T) the gain is 3.3%, 4.4% and 5.5% at Δ = 7, 8,
+    10: the sub-maximal sink P~ fall where 448's coarser top binade matters less. The size is
+    pinned to what the recipe gives; the mechanism behind the printed size is pinned in
+    test_s448_step_excess_over_the_top_octave."""
     mse = _mse_pcast(4096, delta, [("forward", 256.0), ("forward", 448.0)])
     g = mse[("forward", 448.0)] / mse[("forward", 256.0)] - 1.0
-    assert 0.0 < g < 0.20, g
+    assert lo < g < hi, g
+
+
+def test_s448_step_excess_over_the_top_octave():
+    """The d_p mechanism behind the printed 10-15% (technical summary, section 2
+    "Optimization 2", condition 2; section 4, "Scale comparison"): for P~ spread over the
+    top octave (1/2, 1], the mean squared rounding error of E4M3(P~ 448)/448 exceeds that of
+    E4M3(P~ 256)/256 by 11-17%, between a log-uniform and a uniform spread of P~ (brute force
+    with the oracle's codec)."""
+    def ratio(p):
+        err = {S: np.mean((e4m3.round_e4m3(p * S) / S - p) ** 2) for S in (256.0, 448.0)}
+        return err[448.0] / err[256.0]
+    n = 400_001
+    uniform = np.linspace(0.5, 1.0, n)[1:]
+    log_uniform = np.exp2(np.linspace(-1.0, 0.0, n))[1:]
+    assert 1.11 < ratio(log_uniform) < 1.13
+    assert 1.15 < ratio(uniform) < 1.18
 
 
 def test_mse_gain_grows_with_sequence_length():
