@@ -83,6 +83,11 @@ fp8attn::Params make_params(const void* q, const void* k, const void* v, float* 
   p.log2_S = (float)(e2 - 1);
   p.log2e_rsqrt_d = (float)(1.4426950408889634 / sqrt((double)d));
   if (counts) pair_totals(B, H, N, causal, n_sink, &p.pairs, &p.pairs_sink);
+  // one query head per kv head whose K and V (E4M3: 2 N d bytes) fit half an XCD's 4 MB L2
+#ifndef FP8ATTN_HEAD_MAJOR_BYTES
+#define FP8ATTN_HEAD_MAJOR_BYTES (2ll << 20)
+#endif
+  p.head_major = H == Hkv && 2ll * N * d <= FP8ATTN_HEAD_MAJOR_BYTES;
   return p;
 }
 
@@ -162,16 +167,78 @@ int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
   return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
 }
 
+unsigned long long fp8_attn_fwd_exact_qk_workspace_bytes(int B, int Hkv, int N, int d) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return (unsigned long long)B * Hkv * N * d * 2ull;
+}
+
+int fp8_attn_fwd_exact_qk(const void* q, const void* k, const void* v, float* o,
+                          int B, int H, int Hkv, int N, int d,
+                          int causal, int kv_order, float S,
+                          const float* q_descale, const float* k_descale, const float* v_descale,
+                          int n_sink, int denominator, unsigned long long* counts,
+                          void* workspace, unsigned long long workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale || !workspace) return FP8ATTN_EINVAL;
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (d != 64 && d != 128) return FP8ATTN_EUNSUPPORTED;
+  if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
+  if (denominator != FP8ATTN_DENOM_FP32 && denominator != FP8ATTN_DENOM_QUANTIZED) return FP8ATTN_EINVAL;
+  if (workspace_bytes < fp8_attn_fwd_exact_qk_workspace_bytes(B, Hkv, N, d)) return FP8ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    return FP8ATTN_EUNSUPPORTED;
+  fp8attn::Params p = make_params(q, k, v, o, B, H, Hkv, N, d, causal, kv_order, S,
+                                  q_descale, k_descale, v_descale, n_sink, counts, denominator);
+  p.kx = static_cast<const uint8_t*>(workspace);
+  p.exact_qk = 1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8attn::launch_keys_to_bf16(p.k, static_cast<uint8_t*>(workspace), (int64_t)B * Hkv * N * d, s);
+  if (e != hipSuccess) return FP8ATTN_ELAUNCH;
+  const bool pow2 = is_pow2(S);
+  e = counts ? fp8attn::launch_fwd_count(p, d, pow2, s) : fp8attn::launch_fwd(p, d, pow2, s);
+  return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
+}
+
 unsigned long long fp8_attn_decode_workspace_bytes(int B, int H, int d, int n_split) {
   if (B <= 0 || H <= 0 || n_split <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
   return (unsigned long long)B * H * n_split * fp8attn::decode_record_floats(d) * sizeof(float);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks and launch of the split-KV decode with its split records in `workspace` (NULL:
+// the library's static scratch of the current device, whose size is checked here).
+int decode_impl(const void* q, const void* k, const void* v, float* o,
+                int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                const float* q_descale, const float* k_descale, const float* v_descale,
+                int n_split, void* workspace, unsigned long long workspace_bytes, bool /*unused*/,
+                void* stream);
+
+}  // namespace
+
+extern "C" {
+
 int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
                     int B, int H, int Hkv, int N, int d, int kv_order, float S,
                     const float* q_descale, const float* k_descale, const float* v_descale,
                     int n_split, void* workspace, unsigned long long workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale || !workspace) return FP8ATTN_EINVAL;
+  if (!workspace) return FP8ATTN_EINVAL;
+  return decode_impl(q, k, v, o, B, H, Hkv, N, d, kv_order, S, q_descale, k_descale, v_descale, n_split,
+                     workspace, workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* q, const void* k, const void* v, float* o,
+                int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                const float* q_descale, const float* k_descale, const float* v_descale,
+                int n_split, void* workspace, unsigned long long workspace_bytes, bool /*unused*/,
+                void* stream) {
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale) return FP8ATTN_EINVAL;
   if (kv_order == FP8ATTN_KV_REVERSE_SINK_LAST) return FP8ATTN_EINVAL;
   const int st = check_common(B, H, Hkv, N, d, 0, kv_order, S);
   if (st != FP8ATTN_OK) return st;
@@ -205,6 +272,10 @@ int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
   const hipError_t e = fp8attn::launch_decode(p, d, is_pow2(S), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_ELAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
 
 int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
 

@@ -9,7 +9,11 @@
 // ------------------------------
 // * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32
 //   rows. K/V blocks of 64 keys stream through LDS (two stages, double-buffered).
-// * Both GEMMs use v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32).
+// * Both GEMMs use v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32). That instruction
+//   truncates small products inside its adder tree; the exact-Q.K^T variant (QX) forms
+//   S^T on v_mfma_f32_32x32x16_bf16 instead, from keys converted once to bf16 and queries
+//   converted in registers (every E4M3 value is a bf16 value, the products are exact and
+//   the sum is accumulated in fp32), with the same 32x32 result layout.
 // * Q.K^T is computed transposed, S^T = K . Q^T (A = 32 keys of K, B = 32 query rows of
 //   Q), so in the result each lane holds one query row: lane l has query col = l % 32
 //   and, for half = l / 32, the keys 8*(r/4) + 4*half + (r%4), r = 0..15, of each
@@ -32,6 +36,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "kernel_common.h"
 
@@ -41,7 +47,12 @@ namespace {
 // Map the linear workgroup id to (b, h, query tile). Workgroups are dispatched to the
 // 8 XCDs round-robin (id % 8); when the kv heads divide evenly, every XCD gets whole kv
 // heads (all their query heads), so K/V of one head stay in one XCD's L2, and within an
-// XCD the tiles run longest-first for causal masking.
+// XCD the tiles run longest-first for causal masking. The order within an XCD is
+//  * rank-major (by default): tile rank r of every head of the XCD, then rank r + 1, so
+//    that the query heads sharing a kv head read the same K/V blocks at about the same time;
+//  * head-major (p.head_major: one query head per kv head and a head's K/V small enough
+//    for the XCD's 4 MB L2): all tiles of one head, then the next head, so that one head's
+//    K/V stays in L2 while its tiles run instead of many heads' K/V passing through it.
 __device__ __forceinline__ void map_tile(const Params& p, int ntiles, int& b, int& h, int& hk, int& qt) {
   const int G = p.H / p.Hkv;
   const int U = p.B * p.Hkv;
@@ -51,11 +62,18 @@ __device__ __forceinline__ void map_tile(const Params& p, int ntiles, int& b, in
   if ((total & 7) == 0 && (U & 7) == 0) {
     const int xcd = L & 7, slot = L >> 3;
     const int upx = U >> 3;
-    const int per_rank = upx * G;
-    rank = slot / per_rank;
-    const int rem = slot - rank * per_rank;
-    unit = xcd * upx + rem / G;
-    member = rem % G;
+    if (p.head_major) {
+      const int uix = slot / ntiles;
+      rank = slot - uix * ntiles;
+      unit = xcd * upx + uix;
+      member = 0;
+    } else {
+      const int per_rank = upx * G;
+      rank = slot / per_rank;
+      const int rem = slot - rank * per_rank;
+      unit = xcd * upx + rem / G;
+      member = rem % G;
+    }
   } else {
     const int BH = p.B * p.H;
     rank = L / BH;
@@ -76,9 +94,10 @@ __device__ __forceinline__ unsigned bytes_below(int n) {
 
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
 // EXT: the options of fp8_attn_fwd_ex (sink split of block 0, quantized row sum); the
-// launches without them run the kernel compiled without their branches.
-template <int D, bool POW2, bool OUT, bool CNT, bool EXT>
-__global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_kernel(const Params p) {
+// launches without them run the kernel compiled without their branches. QX: Q.K^T on the
+// bf16 matrix cores from the bf16 keys p.kx (d <= 128; two waves per SIMD).
+template <int D, bool POW2, bool OUT, bool CNT, bool EXT, bool QX>
+__global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) void fwd_kernel(const Params p) {
   constexpr int kWaves = waves_for(D);
   constexpr int kThreads = 64 * kWaves;
   constexpr int kBlockM = kRowsPerWave * kWaves;
@@ -91,10 +110,21 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   // staging: one LDS-DMA instruction moves 64 lanes x 16 bytes = 1 KiB of a tile
   constexpr int INST_PER_TILE = TILE / 1024;
   constexpr int RPW = (INST_PER_TILE + kWaves - 1) / kWaves;    // per wave and tile (at most)
+  // K rows: D bytes of E4M3, or 2 D bytes of bf16 (QX), in CHK 16-byte chunks. A bf16 row
+  // of d = 128 fills all 64 banks, so 16 consecutive rows read at one chunk need 16
+  // distinct slots: slot = chunk ^ (row & 15).
+  static_assert(!QX || D <= 128, "the exact Q.K^T variant holds d <= 128");
+  constexpr int KROW = QX ? 2 * D : D;
+  constexpr int CHK = KROW / 16;
+  constexpr int SWZK = !QX ? SWZ : CHK >= 16 ? 15 : (CHK >= 8 ? 8 : CHK) - 1;
+  auto swzk = [](int j) { return SWZK == 15 ? (j & 15) : swz_row<SWZK>(j); };
+  constexpr int TILE_K = kKvBlock * KROW;
+  constexpr int INST_PER_TILE_K = TILE_K / 1024;
+  constexpr int RPWK = (INST_PER_TILE_K + kWaves - 1) / kWaves;
   // Double buffers for K and V, four separate arrays so that the compiler can tell a DMA
   // into one buffer from reads of another: K(n), V(n) are read while block n + 1 lands.
-  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE_K];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE_K];
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[OUT ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[OUT ? TILE : 16];
   auto kbuf = [&](int i) __attribute__((always_inline)) { return i ? kb1 : kb0; };
@@ -121,21 +151,34 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
   const size_t q_head = ((size_t)b * p.H + h) * (size_t)p.N * D;
   const size_t kv_head = ((size_t)b * p.Hkv + hk) * (size_t)p.N * D;
-  const uint8_t* __restrict__ Kg = p.k + kv_head;
+  const uint8_t* __restrict__ Kg = QX ? p.kx + 2 * kv_head : p.k + kv_head;
   const uint8_t* __restrict__ Vg = p.v + kv_head;
 
   // logits in log2 units: s' = raw . c with c = qd kd log2(e) / sqrt(d)
   const float c = p.q_descale[b * p.H + h] * p.k_descale[b * p.Hkv + hk] * p.log2e_rsqrt_d;
 
-  // Q operand (B of S^T = K Q^T): lane (col, half) holds q[r0+col][64m + 32 half .. +32]
-  i32x8 qop[DM];
+  // Q operand (B of S^T = K Q^T): lane (col, half) holds q[r0+col][64m + 32 half .. +32];
+  // QX: the bf16 operand of instruction m, q[r0+col][16m + 8 half .. +8] converted
+  constexpr int MX = D / 16;
+  i32x8 qop[QX ? 1 : DM];
+  i32x4 qopx[QX ? MX : 1];
   if (wave_valid) {
-    const uint8_t* qrow = p.q + q_head + (size_t)(r0 + col) * D + 32 * half;
+    if constexpr (QX) {
+      const uint8_t* qrow = p.q + q_head + (size_t)(r0 + col) * D + 8 * half;
 #pragma unroll
-    for (int m = 0; m < DM; ++m) {
-      const i32x4 lo = *(const i32x4*)(qrow + 64 * m);
-      const i32x4 hi = *(const i32x4*)(qrow + 64 * m + 16);
-      qop[m] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      for (int m = 0; m < MX; ++m) {
+        const i32x2 w = *(const i32x2*)(qrow + 16 * m);
+        const i32x2 lo = e4m3x4_to_bf16x4(w.x), hi = e4m3x4_to_bf16x4(w.y);
+        qopx[m] = i32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+      const uint8_t* qrow = p.q + q_head + (size_t)(r0 + col) * D + 32 * half;
+#pragma unroll
+      for (int m = 0; m < DM; ++m) {
+        const i32x4 lo = *(const i32x4*)(qrow + 64 * m);
+        const i32x4 hi = *(const i32x4*)(qrow + 64 * m + 16);
+        qop[m] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
     }
   }
 
@@ -150,6 +193,16 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 #pragma unroll
     for (int e = 0; e < 2; ++e) koff[m][e] = col * D + (((4 * m + 2 * half + e) ^ swz(col)) << 4);
   auto kaddr = [&](int t, int m, int e) { return koff[m ^ (KT * t)][e] + 32 * t * D; };
+  // QX: the bf16 operand of instruction m for key row 32t + col: chunk 2m + half, slot
+  // (2m + half) ^ swzk(32t + col); with (j & 15) the slot does not depend on t
+  int koffx[QX ? 2 : 1][QX ? MX : 1];
+  if constexpr (QX) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < MX; ++m)
+        koffx[t][m] = (32 * t + col) * KROW + (((2 * m + half) ^ swzk(32 * t + col)) << 4);
+  }
   // V^T operand through the transpose read: within a 16-lane group g, lane sl supplies key
   // row 16 tw + 8 (g >> 1) + (sl >> 1) and 8 columns of output tile u. Adding 16 tw to the
   // row flips swizzle bits 2 tw, i.e. tile u reads like tile u ^ tw.
@@ -174,19 +227,33 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   // at LDS row 16(2t + a/2) + 8h + 4(a%2) + b. So P needs no exchange between lane halves.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto swap23 = [](int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); };
-  int goff[RPW], goffv[RPW];
+  int goff[RPWK], goffv[RPW];
+#pragma unroll
+  for (int r = 0; r < RPWK; ++r) {
+    const int ii = wave + kWaves * r;
+    const int j = (1024 / KROW) * ii + lane / CHK, cs = lane % CHK;
+    goff[r] = j * KROW + ((cs ^ swzk(j)) << 4);
+  }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int ii = wave + kWaves * r;
     const int j = (1024 / D) * ii + lane / CH, cs = lane % CH;
-    goff[r] = j * D + ((cs ^ swz(j)) << 4);
     goffv[r] = swap23(j) * D + ((cs ^ swz(j)) << 4);
   }
-  auto dma_tile = [&](const uint8_t* src, int blk, uint8_t* dst, const int (&off)[RPW]) __attribute__((always_inline)) {
+  // one tile of rows of `row_bytes` bytes (INST instructions of 1 KiB, RPWT per wave)
+  auto dma_rows = [&](const uint8_t* src, int row_bytes, int inst, auto rpwt, int blk, uint8_t* dst,
+                      const int* off) __attribute__((always_inline)) {
+    constexpr int R = decltype(rpwt)::value;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      if (INST_PER_TILE % kWaves == 0 || wave_s + kWaves * r < INST_PER_TILE)
-        lds_dma16(src, p.N * D, dst + (wave_s + kWaves * r) * 1024, off[r], blk * TILE);
+    for (int r = 0; r < R; ++r)
+      if (inst % kWaves == 0 || wave_s + kWaves * r < inst)
+        lds_dma16(src, p.N * row_bytes, dst + (wave_s + kWaves * r) * 1024, off[r], blk * kKvBlock * row_bytes);
+  };
+  auto dma_k = [&](int blk, uint8_t* dst) __attribute__((always_inline)) {
+    dma_rows(Kg, KROW, INST_PER_TILE_K, std::integral_constant<int, RPWK>{}, blk, dst, goff);
+  };
+  auto dma_v = [&](int blk, uint8_t* dst) __attribute__((always_inline)) {
+    dma_rows(Vg, D, INST_PER_TILE, std::integral_constant<int, RPW>{}, blk, dst, goffv);
   };
   // every wave waits for its own DMA, then the barrier publishes all of them
   auto dma_wait_sync = []() __attribute__((always_inline)) {
@@ -213,6 +280,17 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   // LDS latency covers them all; d = 256 has no room for that and pairs each MFMA with
   // its two reads.
   auto qk = [&](const uint8_t* Ks, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    if constexpr (QX) {
+      // 2 tiles x MX bf16 MFMAs; each operand read right before its MFMA
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{0};
+#pragma unroll
+        for (int m = 0; m < MX; ++m)
+          s[t] = mfma_bf16(*(const i32x4*)(Ks + koffx[t][m]), qopx[m], s[t]);
+      }
+      return;
+    }
     auto kop = [&](int t, int m) __attribute__((always_inline)) {
       const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
       const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
@@ -319,7 +397,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         lsum = (t == 0 && a == 0) ? part : lsum + part;
         // (the option-carrying variant keeps no P across blocks: it has no registers to
         // spare for it)
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, EXT ? __builtin_nondeterministic_value(0) : pop[4 * t + a], false);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, EXT ? __builtin_nondeterministic_value(0) : pop[4 * t + a], false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
         pw[4 * t + a] = w;
       }
@@ -409,8 +487,8 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
 
   i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};   // P of the block, in the B-operand layout of the P.V product
   {
-    dma_tile(Kg, block_of(0), kb0, goff);
-    if (OUT) dma_tile(Vg, block_of(0), vb0, goffv);
+    dma_k(block_of(0), kb0);
+    if (OUT) dma_v(block_of(0), vb0);
     dma_wait_sync();
     // step n on buffers `cur` (a constant 0 or 1 at each call site); block n + 1 lands in
     // the other pair
@@ -420,8 +498,8 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
         // in a scalar register (the option-carrying variant otherwise wraps each load in a
         // loop over lanes)
         const int next = __builtin_amdgcn_readfirstlane(block_of(n + 1));
-        dma_tile(Kg, next, kbuf(cur ^ 1), goff);
-        if (OUT) dma_tile(Vg, next, vbuf(cur ^ 1), goffv);
+        dma_k(next, kbuf(cur ^ 1));
+        if (OUT) dma_v(next, vbuf(cur ^ 1));
       }
       if (active(n)) {
         const int blk = block_of(n);
@@ -494,6 +572,16 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), min_waves_per_simd(D)) void fwd_ker
   }
 }
 
+// K (E4M3) -> the same values as bf16, 16 codes per thread.
+__global__ void keys_to_bf16_kernel(const uint8_t* __restrict__ k, uint8_t* __restrict__ kx, int64_t n16) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n16) return;
+  const i32x4 w = ((const i32x4*)k)[t];
+  const i32x2 a = e4m3x4_to_bf16x4(w.x), b = e4m3x4_to_bf16x4(w.y);
+  const i32x2 c = e4m3x4_to_bf16x4(w.z), d = e4m3x4_to_bf16x4(w.w);
+  ((i32x8*)kx)[t] = i32x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 // Zero counts start at 0; the pair counts are known in closed form before the launch.
 __global__ void init_counts_kernel(unsigned long long* counts, unsigned long long pairs,
                                    unsigned long long pairs_sink) {
@@ -505,32 +593,41 @@ __global__ void init_counts_kernel(unsigned long long* counts, unsigned long lon
   }
 }
 
+template <int D, bool OUT, bool CNT, bool EXT, bool QX>
+void launch_one(const Params& p, bool pow2, hipStream_t stream) {
+  const dim3 grid((unsigned)num_workgroups(p, D)), block(64 * waves_for(D));
+  if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT, EXT, QX>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT, EXT, QX>), grid, block, 0, stream, p);
+}
+
+template <int D, bool OUT, bool CNT>
+void launch_d(const Params& p, bool pow2, hipStream_t stream) {
+  const bool ext = p.sink_last || p.qden;
+  if constexpr (D <= 128) {
+    if (p.exact_qk) {
+      if (ext) launch_one<D, OUT, CNT, true, true>(p, pow2, stream);
+      else launch_one<D, OUT, CNT, false, true>(p, pow2, stream);
+      return;
+    }
+  }
+  if (ext) launch_one<D, OUT, CNT, true, false>(p, pow2, stream);
+  else launch_one<D, OUT, CNT, false, false>(p, pow2, stream);
+}
+
 template <bool OUT, bool CNT>
 hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
-  const bool ext = p.sink_last || p.qden;
   if (CNT) {
     hipLaunchKernelGGL(init_counts_kernel, dim3(1), dim3(64), 0, stream, p.counts, p.pairs, p.pairs_sink);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#define FP8ATTN_LAUNCH(D)                                                                       \
-  {                                                                                             \
-    const dim3 grid((unsigned)num_workgroups(p, D)), block(64 * waves_for(D));                  \
-    if (ext) {                                                                                  \
-      if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT, true>), grid, block, 0, stream, p); \
-      else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT, true>), grid, block, 0, stream, p);     \
-    } else {                                                                                    \
-      if (pow2) hipLaunchKernelGGL((fwd_kernel<D, true, OUT, CNT, false>), grid, block, 0, stream, p); \
-      else hipLaunchKernelGGL((fwd_kernel<D, false, OUT, CNT, false>), grid, block, 0, stream, p);     \
-    }                                                                                           \
-  }
+  if (p.exact_qk && d > 128) return hipErrorInvalidValue;
   switch (d) {
-    case 64: FP8ATTN_LAUNCH(64) break;
-    case 128: FP8ATTN_LAUNCH(128) break;
-    case 256: FP8ATTN_LAUNCH(256) break;
+    case 64: launch_d<64, OUT, CNT>(p, pow2, stream); break;
+    case 128: launch_d<128, OUT, CNT>(p, pow2, stream); break;
+    case 256: launch_d<256, OUT, CNT>(p, pow2, stream); break;
     default: return hipErrorInvalidValue;
   }
-#undef FP8ATTN_LAUNCH
   return hipGetLastError();
 }
 
@@ -538,6 +635,15 @@ hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
   return launch<true, false>(p, d, pow2_scale, stream);
+}
+
+hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, hipStream_t stream) {
+  const int64_t n16 = n_elements / 16;
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(keys_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, kx, n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream) {

@@ -21,6 +21,26 @@ __device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, cons
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// bf16 x bf16 -> fp32, 32x32 outputs, k = 16 (exact products, fp32 accumulation); the
+// result layout is the one of mfma_e4m3.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16 mfma_bf16(const i32x4& a, const i32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Two E4M3 codes (the low or the high 16-bit word of w) to two bf16 values, exactly (every
+// E4M3 value is a bf16 value); one packed word.
+template <bool HI>
+__device__ __forceinline__ int e4m3x2_to_bf16x2(int w) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Four E4M3 codes (one dword) to four bf16 values (two dwords), in the same order.
+__device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int w) {
+  return i32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS row swizzle: 16-byte chunk c of row j lives at chunk c ^ swz(j). With

@@ -9,6 +9,7 @@ namespace fp8attn {
 struct Params {
   const uint8_t* q;                 // [B][H][N][d] E4M3
   const uint8_t* k;                 // [B][Hkv][N][d] E4M3
+  const uint8_t* kx;                // [B][Hkv][N][d] the same keys as bf16 (exact Q.K^T launches)
   const uint8_t* v;                 // [B][Hkv][N][d] E4M3 (unused by a count-only launch)
   float* o;                         // [B][H][N][d] fp32 (unused by a count-only launch)
   const float* q_descale;           // [B*H]
@@ -21,6 +22,8 @@ struct Params {
   int causal, reverse, n_sink;
   int sink_last;                    // reverse walk, block 0 as [n_sink, 64) then [0, n_sink)
   int qden;                         // row sum of the decoded cast operand (else of P~ S)
+  int exact_qk;                     // Q.K^T on the bf16 matrix cores from kx (exact products)
+  int head_major;                   // grid order within an XCD: all tiles of a head together
   float S;                          // static P scale
   float log2_S;                     // exact log2(S) when S is a power of two
   float log2e_rsqrt_d;              // log2(e)/sqrt(d), rounded once to fp32
@@ -64,6 +67,8 @@ struct DecodeParams {
 constexpr int decode_record_floats(int d) { return d + 4; }
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream);
+// K [B][Hkv][N][d] E4M3 -> kx, the same values as bf16 (exact), for the exact Q.K^T launches
+hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_fwd_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);

@@ -56,10 +56,22 @@ def oracle(inp, *, causal, order, S, rows=None, heads=None, counts=False, n_sink
                                            with_counts=counts, denominator=denominator, qk_accumulation=qk)
 
 
-def check_output(o_gpu, ref, label="", qk=None):
+def s_on_a_midpoint(S):
+    """True if S lies within the fp32 band of an E4M3 rounding midpoint: then every row's
+    maximum (P~ = 1, cast S) is a legitimate tie that the device may round either way, and
+    the fraction of rows beyond O_TOL says nothing (S = 100 lies between 96 and 104)."""
+    from oracle import e4m3
+
+    vals = e4m3.all_finite_values()
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    return bool((np.abs(S - mids) <= oracle_attention.FLIP_REL_WINDOW * mids).any())
+
+
+def check_output(o_gpu, ref, label="", qk=None, S=None):
     """o_gpu: full [B,H,N,d] device tensor; ref: oracle dict (heads x rows). Every element
     within O_TOL plus its allowance; with ``qk`` (an exact-logit reference) also the row
-    fraction beyond O_TOL and the largest deviation within their limits."""
+    fraction beyond O_TOL (unless S sits on a midpoint) and the largest deviation within
+    their limits."""
     got = np.stack([o_gpu[b, h].cpu().numpy()[ref["rows"]] for (b, h) in ref["heads"]])
     diff = np.abs(got - ref["o"])
     excess = diff - (O_TOL + ref["allow"])
@@ -70,7 +82,10 @@ def check_output(o_gpu, ref, label="", qk=None):
     assert np.isfinite(got).all(), "non-finite output"
     assert excess.max() <= 0, f"{label}: output exceeds tolerance by {excess.max():.3g}"
     if qk is not None:
-        assert beyond.mean() <= ROWS_BEYOND_LIMIT[qk], f"{label}: {beyond.mean():.4f} of rows beyond {O_TOL}"
+        if S is not None and s_on_a_midpoint(S):
+            say(f"  (S = {S} lies on an E4M3 rounding midpoint: every row maximum is a tie; no row-fraction limit)")
+        else:
+            assert beyond.mean() <= ROWS_BEYOND_LIMIT[qk], f"{label}: {beyond.mean():.4f} of rows beyond {O_TOL}"
         assert diff.max() <= MAX_DEV_LIMIT, f"{label}: max|dO| {diff.max():.3g}"
     return diff.max()
 
@@ -96,7 +111,7 @@ def check_both(inp, o, c, *, causal, order, S, label, rows=None, heads=None, cou
     for logits, primary in refs:
         ref = oracle(inp, causal=causal, order=order, S=S, rows=rows, heads=heads, logits=logits,
                      counts=c is not None and count_heads is None, **opts)
-        check_output(o, ref, f"{label} [{logits} logits]", qk=qk if primary else None)
+        check_output(o, ref, f"{label} [{logits} logits]", qk=qk if primary else None, S=S)
         if c is not None:
             cref = ref if count_heads is None else oracle(inp, causal=causal, order=order, S=S, heads=count_heads,
                                                           logits=logits, counts=True, **opts)

@@ -22,6 +22,12 @@ int hw_probe_cvt_e4m3(const float* in, unsigned char* out, long n, void* stream)
 int hw_probe_mfma_dots(const unsigned char* a, const unsigned char* b, float* raw, int T, int kch,
                        void* stream);
 
+/* raw[t][i][j] = sum_c a[t][i][c] * b[t][j][c] over c < K (a multiple of 16), computed by
+ * K/16 chained v_mfma_f32_32x32x16_bf16; a, b: [T][32][K] bf16 bit patterns (16-byte
+ * aligned), raw: [T][32][32] fp32. */
+int hw_probe_mfma_bf16_dots(const unsigned short* a, const unsigned short* b, float* raw, int T, int K,
+                            void* stream);
+
 /* Throughput kernel for the roofline denominators. Each of `blocks` workgroups of 512
  * threads (8 waves, 2 per SIMD) runs `iters` iterations of
  *   kind 0: 8 v_mfma_f32_32x32x64_f8f6f4 on 4 independent accumulators (131072 FLOP each);

@@ -41,6 +41,25 @@ __global__ void mfma_kernel(const uint8_t* a, const uint8_t* b, float* raw, int 
   }
 }
 
+// bf16 form: one wave per problem t; a, b: [T][32][K] bf16 bits; k-slots 16m + 8h .. +7
+// of instruction m for lane half h; same result layout as mfma_kernel.
+__global__ void mfma_bf16_kernel(const uint16_t* a, const uint16_t* b, float* raw, int K) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int t = blockIdx.x, l = threadIdx.x;
+  const int r = l & 31, h = l >> 5;
+  f32x16 acc = {0};
+  for (int m = 0; m < K / 16; ++m) {
+    const i32x4 av = *(const i32x4*)(a + ((size_t)t * 32 + r) * K + 16 * m + 8 * h);
+    const i32x4 bv = *(const i32x4*)(b + ((size_t)t * 32 + r) * K + 16 * m + 8 * h);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                  acc, 0, 0, 0);
+  }
+  for (int q = 0; q < 16; ++q) {
+    const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+    raw[((size_t)t * 32 + row) * 32 + r] = acc[q];
+  }
+}
+
 __global__ __launch_bounds__(512) void throughput_kernel(int kind, int iters, const int* seed, float* sink,
                                                          float* clock) {
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -92,6 +111,14 @@ extern "C" int hw_probe_throughput(int kind, int blocks, int iters, const int* s
   if (kind < 0 || kind > 3 || blocks <= 0 || iters <= 0 || !seed || !sink || !clock) return -1;
   hipLaunchKernelGGL(throughput_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, kind, iters, seed,
                      sink, clock);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hw_probe_mfma_bf16_dots(const unsigned short* a, const unsigned short* b, float* raw, int T, int K,
+                                       void* stream) {
+  if (!a || !b || !raw || T <= 0 || K <= 0 || K % 16 || K > 4096) return -1;
+  if ((((uintptr_t)a) | ((uintptr_t)b)) & 15) return -1;
+  hipLaunchKernelGGL(mfma_bf16_kernel, dim3(T), dim3(64), 0, (hipStream_t)stream, a, b, raw, K);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

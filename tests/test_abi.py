@@ -153,3 +153,40 @@ def test_product_path_does_not_import_the_oracle():
         if path.endswith((".py", ".hip", ".h", ".cpp")):
             src = open(path).read()
             assert not re.search(r"^\s*(from\s+oracle\b|import\s+oracle\b)|\boracle\.", src, re.M), path
+
+
+def test_binding_tensor_checks_on_cpu():
+    """The binding's one check for every tensor it hands to the library refuses host
+    tensors, wrong dtypes, shapes, element counts and short buffers (no GPU needed: the
+    expected device is named, never touched)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    ok_kw = dict(shape=(2, 3))
+    with pytest.raises(ValueError, match="on cpu"):
+        binding._check_tensor(torch.zeros(2, 3), "out", dev, torch.float32, **ok_kw)
+    with pytest.raises(ValueError, match="expected a torch tensor"):
+        binding._check_tensor([0.0] * 6, "out", dev, torch.float32, **ok_kw)
+    meta = torch.empty(2, 3, device="meta")
+    with pytest.raises(ValueError):
+        binding._check_tensor(meta, "out", dev, torch.float32, **ok_kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), -1), (dict(ws_bytes=1), -1), (dict(d=256), -2), (dict(d=96), -2),
+    (dict(order=3), -1), (dict(den=2), -1), (dict(n_sink=65, order=2), -1), (dict(ws=FAKE + 8), -2),
+    (dict(S=449.0), -1), (dict(N=100), -2),
+])
+def test_exact_qk_validation(lib, kw, status):
+    a = dict(B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=1, S=256.0, n_sink=4, den=0, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    rc = lib.fp8_attn_fwd_exact_qk(FAKE, FAKE, FAKE, FAKE, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                   a["order"], a["S"], FAKE, FAKE, FAKE, a["n_sink"], a["den"], None, a["ws"],
+                                   a["ws_bytes"], None)
+    assert rc == status
+
+
+def test_exact_qk_workspace_bytes(lib):
+    assert lib.fp8_attn_fwd_exact_qk_workspace_bytes(2, 8, 4096, 128) == 2 * 8 * 4096 * 128 * 2
+    assert lib.fp8_attn_fwd_exact_qk_workspace_bytes(1, 1, 64, 256) == 0
+

@@ -3,10 +3,11 @@
 * The E4M3 codec: v_cvt_pk_fp8_f32 (the instruction the kernel casts P·S with) must give
   the oracle's round-to-nearest-even code for every |x| < 464 (beyond that the
   instruction returns NaN; P·S never exceeds 448).
-* The matrix-core model used for the parity tolerance: v_mfma_f32_32x32x64_f8f6f4 on
-  random sink-shaped E4M3 operands must match ``oracle.mfma_model`` bit for bit (a rare
-  last-ulp difference is allowed: the model's handling of group-sum truncation is an
-  approximation at the fp32 rounding level).
+* The matrix core's accumulation: v_mfma_f32_32x32x64_f8f6f4 on random E4M3 operands
+  must stay within the error bound the exact-logit parity tolerance is built from
+  (``oracle.mfma_model.error_bound``), and match the point model of the same rule bit for
+  bit (a rare last-ulp difference is allowed: the model's handling of group-sum truncation
+  is an approximation at the fp32 rounding level).
 """
 import ctypes
 import os
@@ -31,6 +32,7 @@ def probe():
     lib.hw_probe_cvt_e4m3.argtypes = [vp, vp, ctypes.c_long, vp]
     lib.hw_probe_mfma_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.hw_probe_throughput.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.hw_probe_mfma_bf16_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     return lib
 
 
@@ -61,34 +63,88 @@ def test_hardware_cvt_matches_oracle_codec(probe):
     assert not bad.any(), (x[bad][:8], hw[bad][:8], ref[bad][:8])
 
 
-@pytest.mark.parametrize("kch", [1, 2, 4])
-def test_hardware_mfma_matches_accumulation_model(probe, kch):
+@pytest.mark.parametrize("kch,kind", [(1, "sink"), (2, "sink"), (4, "sink"), (2, "uniform")])
+def test_hardware_mfma_matches_accumulation_model(probe, kch, kind):
+    """The instruction against the stated rule: always within the error bound that the
+    exact-logit parity tolerance is built from; on sink-shaped data bit for bit with the
+    point model (a rare last-ulp difference allowed). "uniform" draws every finite code
+    with equal weight, so the exponents in a group span the whole E4M3 range; there the
+    point model is only approximate at the fp32 level of the result."""
     T, K = 96, 64 * kch
-    rng = np.random.default_rng(kch)
-    scale = rng.choice([20.0, 60.0, 140.0], size=(T, 1, 1))
-    a = rng.standard_normal((T, 32, K)) * scale
-    b = rng.standard_normal((T, 32, K)) * scale
-    a[:, :, 0] = 448.0
-    b[:, :4, 0] = 448.0
-    b[:, 4:, 0] = rng.standard_normal((T, 28)) * 300
-    a8 = e4m3.encode(np.clip(a, -448, 448))
-    b8 = e4m3.encode(np.clip(b, -448, 448))
-    say(f"case hw mfma vs model kch={kch}")
+    rng = np.random.default_rng(kch + (100 if kind == "uniform" else 0))
+    if kind == "sink":
+        scale = rng.choice([20.0, 60.0, 140.0], size=(T, 1, 1))
+        a = rng.standard_normal((T, 32, K)) * scale
+        b = rng.standard_normal((T, 32, K)) * scale
+        a[:, :, 0] = 448.0
+        b[:, :4, 0] = 448.0
+        b[:, 4:, 0] = rng.standard_normal((T, 28)) * 300
+        a8 = e4m3.encode(np.clip(a, -448, 448))
+        b8 = e4m3.encode(np.clip(b, -448, 448))
+    else:
+        finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        a8 = rng.choice(finite, size=(T, 32, K))
+        b8 = rng.choice(finite, size=(T, 32, K))
+    say(f"case hw mfma vs model kch={kch} {kind}")
     dev = device()
-    ta = torch.from_numpy(a8).to(dev)
-    tb = torch.from_numpy(b8).to(dev)
+    ta = torch.from_numpy(np.ascontiguousarray(a8)).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(b8)).to(dev)
     raw = torch.empty((T, 32, 32), dtype=torch.float32, device=dev)
     assert probe.hw_probe_mfma_dots(ta.data_ptr(), tb.data_ptr(), raw.data_ptr(), T, kch, None) == 0
     torch.cuda.synchronize()
     hw = raw.cpu().numpy().astype(np.float64)
     model = np.stack([mfma_model.model_dots(a8[t], b8[t]) for t in range(T)])
+    bound = np.stack([mfma_model.error_bound(a8[t], b8[t]) for t in range(T)])
     exact = np.einsum("tik,tjk->tij", e4m3.decode(a8), e4m3.decode(b8))
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(hw), 1e-30))) - 23)
     same = hw == model
     say(f"  bit-exact {same.mean():.6f}; max|hw-model| {np.abs(hw - model).max():.3g}; "
-        f"max|hw-exact| {np.abs(hw - exact).max():.3g}")
-    assert same.mean() >= 0.999
-    assert (np.abs(hw - model) <= ulp).all()
+        f"max|hw-exact| {np.abs(hw - exact).max():.3g}; max |hw-exact|/bound {(np.abs(hw - exact) / bound).max():.3f}")
+    assert (np.abs(hw - exact) <= bound).all()
+    if kind == "sink":
+        assert same.mean() >= 0.999
+        assert (np.abs(hw - model) <= ulp).all()
+    # with every exponent present the point model is only approximate (85% bit for bit,
+    # off by up to 2^-4 absolute, at the scale of the group-sum rounding of the largest
+    # products); the tolerance uses the bound, never the point model
+
+
+@pytest.mark.parametrize("kind", ["sink", "uniform"])
+def test_hardware_bf16_mfma_is_exact_within_fp32_accumulation(probe, kind):
+    """The exact Q.K^T variant's premise: v_mfma_f32_32x32x16_bf16 on E4M3 values (held
+    exactly in bf16) forms the products exactly and accumulates in fp32, so its dot
+    products stay within oracle.mfma_model.fp32_accumulation_bound (one fp32 rounding per
+    16-slot instruction) of the exact ones, where the FP8 instruction does not."""
+    T, K = 64, 128
+    rng = np.random.default_rng(7 + (kind == "uniform"))
+    if kind == "sink":
+        a = rng.standard_normal((T, 32, K)) * 60
+        b = rng.standard_normal((T, 32, K)) * 60
+        a[:, :, 0] = 448.0
+        b[:, :4, 0] = 448.0
+        a8 = e4m3.encode(np.clip(a, -448, 448))
+        b8 = e4m3.encode(np.clip(b, -448, 448))
+    else:
+        finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        a8 = rng.choice(finite, size=(T, 32, K))
+        b8 = rng.choice(finite, size=(T, 32, K))
+    say(f"case hw bf16 mfma exactness {kind}")
+    bits = lambda c: (e4m3.decode(c).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bits(a8).astype(np.uint32) << 16, e4m3.decode(a8).astype(np.float32).view(np.uint32))
+    dev = device()
+    ta = torch.from_numpy(np.ascontiguousarray(bits(a8)).view(np.int16)).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(bits(b8)).view(np.int16)).to(dev)
+    raw = torch.empty((T, 32, 32), dtype=torch.float32, device=dev)
+    assert probe.hw_probe_mfma_bf16_dots(ta.data_ptr(), tb.data_ptr(), raw.data_ptr(), T, K, None) == 0
+    torch.cuda.synchronize()
+    hw = raw.cpu().numpy().astype(np.float64)
+    exact = np.einsum("tik,tjk->tij", e4m3.decode(a8), e4m3.decode(b8))
+    bound = np.stack([mfma_model.fp32_accumulation_bound(a8[t], b8[t]) for t in range(T)])
+    fp8_bound = np.stack([mfma_model.error_bound(a8[t], b8[t]) for t in range(T)])
+    say(f"  max|hw-exact| {np.abs(hw - exact).max():.3g}; max ratio to the fp32 bound "
+        f"{(np.abs(hw - exact) / bound).max():.3f}; median FP8-path bound / fp32 bound "
+        f"{np.median(fp8_bound / bound):.0f}")
+    assert (np.abs(hw - exact) <= bound).all()
 
 
 def test_throughput_roofline_denominators(probe):
