@@ -22,21 +22,11 @@ def test_records_follow_the_source_hash(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "abc")
     assert bench.measured_traffic(WL) is None
-    assert bench.measured_sq(WL, 1000.0) == (None, None)
-    sq = {"kernel_source_hash": "abc", "mfma_flop_per_clk_per_cu": 8000, "sclk_ghz": 2.0,
-          "valu_busy_frac": 0.7, "valu_per_wave_step": 190.0, "mfma_per_wave_step": 8.0,
-          "mfma_busy_frac": 0.4, "coexec_frac_of_mfma": 0.6}
     _write(tmp_path, f"traffic_fwd_counted_{WL}.json", {"kernel_source_hash": "abc", "hbm_bytes_per_launch": 123})
-    _write(tmp_path, f"sq_fwd_counted_{WL}.json", sq)
     assert bench.measured_traffic(WL) == 123
-    clock, valu = bench.measured_sq(WL, 2048.0)
-    assert clock["peak"] == pytest.approx(256 * 8000 * 2.0e9 / 1e12)
-    assert clock["frac"] == pytest.approx(2048.0 / clock["peak"])
-    assert valu["bound"] == "valu" and valu["busy_frac"] == 0.7
     # a record of another kernel source is not reported
     monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "def")
     assert bench.measured_traffic(WL) is None
-    assert bench.measured_sq(WL, 2048.0) == (None, None)
 
 
 def test_committed_traffic_record_is_consistent():

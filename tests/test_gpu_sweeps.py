@@ -10,6 +10,11 @@ that survive E4M3 quantisation of Q, K and V (the pages measure with Q, K, V in 
   collapses and much worse where P collapses: the collapsed mass leaves the denominator
   too, so the sinks take the weight.
 * The sink-last schedule changes the error of clean inputs by less than 1%.
+* S = 256 against S = 384 and 448 in forward order, measured on the error the P cast adds
+  (the GPU output against attention of the same E4M3 operands without the cast, the
+  quantity the pages' comparison is about: section 4, "Scale comparison"). The size of the
+  gain depends on where the large P~ fall within an octave; on this recipe the oracle gives
+  3-6%, the pages print 10-15% for their own, unstated, P distribution.
 Every measured table is printed (``-s`` shows it).
 """
 import numpy as np
@@ -17,6 +22,7 @@ import pytest
 import torch
 
 from oracle import attention as A
+from oracle import e4m3
 from precision_attention_amd import binding
 from precision_attention_amd import inputs as I
 
@@ -92,3 +98,37 @@ def test_sink_last_keeps_the_error_of_clean_inputs():
     last = _mse(t, rows, ref, order="reverse_sink_last", S=256.0)
     say(f"  reverse {rev:.5e}  sink-last {last:.5e}")
     assert abs(last / rev - 1.0) < 0.01
+
+
+@pytest.mark.parametrize("delta", [7.0, 8.0, 10.0])
+def test_s256_against_s384_and_s448(delta):
+    """MSE of the P cast alone (against exact attention of the dequantized E4M3 operands,
+    no cast) on the GPU path for S = 256, 384 and 448, forward order, 1024 rows of each of
+    two heads. The gains of 384 and 448 over 256 must match the oracle's on the same rows
+    (within 3 points); whether 256 wins is printed. With E4M3 Q, K, V the large P~ fall
+    differently within an octave than with the pages' fp32 operands, and the oracle itself
+    has 448 ahead at some Δ (the fp32-operand case, where 256 wins by 3-6%, is pinned on the
+    CPU)."""
+    N = 4096
+    inp, t, rows, _ = _setup(N, delta, n_rows=1024)
+    refs, heads = [], []
+    for h in range(HEADS):
+        s8, _ = A.head_logits_e4m3(inp["q8"][0, h], inp["k8"][0, h], inp["qd"][0, h], inp["kd"][0, h], D, rows=rows)
+        vf = e4m3.decode(inp["v8"][0, h]) * float(inp["vd"][0, h])
+        refs.append(A.exact_attention(s8, vf))
+        heads.append((s8, vf))
+    ref = np.stack(refs)
+    say(f"case S=256 vs 384/448 (P-cast error), forward, N={N} delta={delta}")
+    scales = (256.0, 384.0, 448.0)
+    mse = {S: _mse(t, rows, ref, order="forward", S=S) for S in scales}
+    mse_o = {}
+    for S in scales:
+        outs = [A.online_softmax_pcast(s8, vf, kv_order="forward", S=S)[0] for (s8, vf) in heads]
+        mse_o[S] = float(np.mean((np.stack(outs) - ref) ** 2))
+    gain = {S: mse[S] / mse[256.0] - 1.0 for S in scales[1:]}
+    gain_o = {S: mse_o[S] / mse_o[256.0] - 1.0 for S in scales[1:]}
+    say(f"  GPU MSE S=256 {mse[256.0]:.5e}  S=384 {100 * gain[384.0]:+.1f}%  S=448 {100 * gain[448.0]:+.1f}% | "
+        f"oracle S=384 {100 * gain_o[384.0]:+.1f}%  S=448 {100 * gain_o[448.0]:+.1f}% | "
+        f"S=256 lowest: {'yes' if min(gain.values()) > 0 else 'no'}")
+    for S in scales[1:]:
+        assert abs(gain[S] - gain_o[S]) <= 0.03, (S, gain[S], gain_o[S])
