@@ -64,7 +64,9 @@ typedef enum {
   FP8ATTN_EUNSUPPORTED = -2, /* d not in {64,128,256}, N % 64 != 0, N*d > 2^31-1,
                                 pointer not 16-byte aligned, grid larger than 2^31-1
                                 workgroups */
-  FP8ATTN_ELAUNCH = -3       /* HIP reported an error for the launch */
+  FP8ATTN_ELAUNCH = -3,      /* HIP reported an error for the launch */
+  FP8ATTN_ESCRATCH = -4      /* fp8_attn_decode_static: the split records need more than
+                                FP8ATTN_STATIC_SCRATCH_BYTES */
 } fp8attn_status;
 
 enum { FP8ATTN_KV_FORWARD = 0, FP8ATTN_KV_REVERSE = 1, FP8ATTN_KV_REVERSE_SINK_LAST = 2 };
@@ -168,6 +170,25 @@ int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
                     int B, int H, int Hkv, int N, int d, int kv_order, float S,
                     const float* q_descale, const float* k_descale, const float* v_descale,
                     int n_split, void* workspace, unsigned long long workspace_bytes, void* stream);
+
+/* fp8_attn_decode for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation, arguments and
+ * errors, with the split records held in a static device array of the library instead of
+ * a caller workspace. Nothing is allocated (no hipMalloc, hipFree or allocating library
+ * routine); the array, FP8ATTN_STATIC_SCRATCH_BYTES per GPU, is part of the library's code
+ * object and held by every GPU it runs on until the process ends.
+ *   Uses the array of the current device (the stream must belong to it); its device address
+ *   is looked up once per device, on the first call there.
+ *   FP8ATTN_ESCRATCH if fp8_attn_decode_workspace_bytes(B, H, d, n_split) exceeds
+ *   FP8ATTN_STATIC_SCRATCH_BYTES (nothing launched).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   (other streams, other threads) race and give undefined results; calls in one stream are
+ *   ordered. No record needs clearing: each call writes every record it reads. */
+#define FP8ATTN_STATIC_SCRATCH_BYTES (8u << 20)
+int fp8_attn_decode_static(const void* q, const void* k, const void* v, float* o,
+                           int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                           const float* q_descale, const float* k_descale, const float* v_descale,
+                           int n_split, void* stream);
 
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);

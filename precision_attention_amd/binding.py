@@ -40,6 +40,8 @@ def _declare(lib):
     lib.fp8_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp, ctypes.c_ulonglong,
                                     vp]
     lib.fp8_attn_decode.restype = i
+    lib.fp8_attn_decode_static.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp]
+    lib.fp8_attn_decode_static.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -317,6 +319,39 @@ def decode(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reve
                              int(n_split), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                              _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_decode")
+    return out
+
+
+def decode_static(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reverse", S: float = 256.0,
+                  n_split: int | None = None, out=None, stream=None):
+    """``decode`` with the split records in the library's static per-GPU scratch
+    (fp8_attn_decode_static: no workspace; calls overlapping on one GPU race)."""
+    import torch
+
+    lib = load()
+    q8, k8, v8 = _as_codes(q8, "q"), _as_codes(k8, "k"), _as_codes(v8, "v")
+    if q8.dim() != 3 or k8.dim() != 4 or tuple(v8.shape) != tuple(k8.shape):
+        raise ValueError("q must be [B, H, d], k and v [B, Hkv, N, d]")
+    B, H, d = q8.shape
+    Bk, Hkv, N, dk = k8.shape
+    if (Bk, dk) != (B, d):
+        raise ValueError(f"k shape {tuple(k8.shape)} does not match q {tuple(q8.shape)}")
+    dev = q8.device
+    for name, t in (("k", k8), ("v", v8)):
+        if t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, expected {dev} (the device of q)")
+    qd = _as_descale(q_descale, B * H, "q_descale", dev)
+    kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
+    vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
+    if n_split is None:
+        n_split = decode_default_splits(B, Hkv, H, N)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _check_tensor(out, "out", dev, torch.float32, shape=(B, H, d))
+    rc = lib.fp8_attn_decode_static(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), B, H, Hkv, N, d,
+                                    KV_ORDERS[kv_order], float(S), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                    int(n_split), _stream_ptr(dev, stream))
+    _status(rc, "fp8_attn_decode_static")
     return out
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fp8attn.h"
 #include "launch.h"
 
@@ -213,7 +215,7 @@ namespace {
 int decode_impl(const void* q, const void* k, const void* v, float* o,
                 int B, int H, int Hkv, int N, int d, int kv_order, float S,
                 const float* q_descale, const float* k_descale, const float* v_descale,
-                int n_split, void* workspace, unsigned long long workspace_bytes, bool /*unused*/,
+                int n_split, void* workspace, unsigned long long workspace_bytes, bool static_scratch,
                 void* stream);
 
 }  // namespace
@@ -229,14 +231,44 @@ int fp8_attn_decode(const void* q, const void* k, const void* v, float* o,
                      workspace, workspace_bytes, false, stream);
 }
 
+int fp8_attn_decode_static(const void* q, const void* k, const void* v, float* o,
+                           int B, int H, int Hkv, int N, int d, int kv_order, float S,
+                           const float* q_descale, const float* k_descale, const float* v_descale,
+                           int n_split, void* stream) {
+  return decode_impl(q, k, v, o, B, H, Hkv, N, d, kv_order, S, q_descale, k_descale, v_descale, n_split,
+                     nullptr, 0, true, stream);
+}
+
 }  // extern "C"
 
 namespace {
 
+// The static scratch of fp8_attn_decode_static: one array per GPU the library runs on,
+// held until the process ends. In host code its name is a host-side stand-in, never a
+// device address: the device address is looked up once per device (with that device
+// current) and only that address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[FP8ATTN_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or NULL if it cannot be found.
+void* current_device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 int decode_impl(const void* q, const void* k, const void* v, float* o,
                 int B, int H, int Hkv, int N, int d, int kv_order, float S,
                 const float* q_descale, const float* k_descale, const float* v_descale,
-                int n_split, void* workspace, unsigned long long workspace_bytes, bool /*unused*/,
+                int n_split, void* workspace, unsigned long long workspace_bytes, bool static_scratch,
                 void* stream) {
   if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale) return FP8ATTN_EINVAL;
   if (kv_order == FP8ATTN_KV_REVERSE_SINK_LAST) return FP8ATTN_EINVAL;
@@ -244,13 +276,21 @@ int decode_impl(const void* q, const void* k, const void* v, float* o,
   if (st != FP8ATTN_OK) return st;
   if (n_split < 1 || n_split > N / fp8attn::kKvBlock) return FP8ATTN_EINVAL;
   const unsigned long long need = fp8_attn_decode_workspace_bytes(B, H, d, n_split);
-  if (workspace_bytes < need) return FP8ATTN_EINVAL;
+  if (static_scratch) {
+    if (need > FP8ATTN_STATIC_SCRATCH_BYTES) return FP8ATTN_ESCRATCH;
+  } else if (workspace_bytes < need) {
+    return FP8ATTN_EINVAL;
+  }
   const int G = H / Hkv;
   const int n_qgroups = (G + 31) / 32;
   if ((int64_t)B * Hkv * n_qgroups * n_split > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
   if ((int64_t)B * H > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (!static_scratch && !aligned16(workspace)))
     return FP8ATTN_EUNSUPPORTED;
+  if (static_scratch) {
+    workspace = current_device_scratch();
+    if (!workspace) return FP8ATTN_ELAUNCH;
+  }
   fp8attn::DecodeParams p{};
   p.q = static_cast<const uint8_t*>(q);
   p.k = static_cast<const uint8_t*>(k);
@@ -287,6 +327,7 @@ const char* fp8_attn_status_string(int status) {
     case FP8ATTN_EINVAL: return "invalid argument";
     case FP8ATTN_EUNSUPPORTED: return "unsupported shape or alignment";
     case FP8ATTN_ELAUNCH: return "kernel launch failed";
+    case FP8ATTN_ESCRATCH: return "request exceeds the static scratch of fp8_attn_decode_static";
     default: return "unknown status";
   }
 }

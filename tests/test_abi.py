@@ -190,3 +190,16 @@ def test_exact_qk_workspace_bytes(lib):
     assert lib.fp8_attn_fwd_exact_qk_workspace_bytes(2, 8, 4096, 128) == 2 * 8 * 4096 * 128 * 2
     assert lib.fp8_attn_fwd_exact_qk_workspace_bytes(1, 1, 64, 256) == 0
 
+
+def test_decode_static_validation(lib):
+    """fp8_attn_decode_static checks its arguments before any HIP call, and refuses split
+    records beyond its static array (B=8, H=64, d=256, 64 splits: 34 MB > 8 MiB)."""
+    call = lambda **kw: lib.fp8_attn_decode_static(
+        kw.get("q", FAKE), FAKE, FAKE, FAKE, kw.get("B", 1), kw.get("H", 8), kw.get("Hkv", 2), kw.get("N", 4096),
+        kw.get("d", 128), kw.get("order", 1), kw.get("S", 256.0), FAKE, FAKE, FAKE, kw.get("n_split", 8), None)
+    assert call(q=None) == -1
+    assert call(order=2) == -1
+    assert call(n_split=0) == -1 and call(n_split=65) == -1
+    assert call(d=96) == -2
+    assert call(B=8, H=64, Hkv=64, N=64 * 64, d=256, n_split=64) == -4
+    assert lib.fp8_attn_status_string(-4).startswith(b"request exceeds")
