@@ -247,7 +247,7 @@ def main():
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": flop / (ms_per_step * 1e-3) / 1e12, "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": flop / (ms_per_step * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                "traffic": traffic, "kernel": "fwd_kernel<128,pow2,out,count>",
+                "traffic": traffic, "kernel": f"fwd_kernel<{w.d}, true, true, true, false, false>",
                 "flop_per_launch": flop}
 
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

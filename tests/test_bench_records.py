@@ -62,7 +62,11 @@ def test_committed_sq_record_is_consistent():
     # 8 MFMAs per wave-step (4 for S, 4 for P.V at d = 128), 64 cycles each
     assert rec["mfma_per_wave_step"] == pytest.approx(8.0)
     assert c["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(64 * c["SQ_INSTS_MFMA"], rel=0.01)
-    assert 0.0 < rec["coexec_frac_of_mfma"] <= 1.0 and 0.0 < rec["valu_busy_frac"] <= 1.0
+    assert 0.0 < rec["coexec_frac_of_mfma"] <= 1.0
+    # the vector-ALU share of the modelled vector work per wave-step over the launch's SIMD cycles
+    assert rec["valu_busy_frac_model"] == pytest.approx(
+        rec["valu_cycles_per_wave_step_model"] * rec["wave_steps_per_launch"] / 1024 / cycles, rel=1e-3)
+    assert 0.0 < rec["valu_busy_frac_model"] <= 1.0
     for cmd in rec["commands"]:
         assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
 
