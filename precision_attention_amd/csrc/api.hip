@@ -194,7 +194,7 @@ int fp8_attn_fwd_exact_qk(const void* q, const void* k, const void* v, float* o,
   p.kx = static_cast<const uint8_t*>(workspace);
   p.exact_qk = 1;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8attn::launch_keys_to_bf16(p.k, static_cast<uint8_t*>(workspace), (int64_t)B * Hkv * N * d, s);
+  hipError_t e = fp8attn::launch_keys_to_bf16(p.k, static_cast<uint8_t*>(workspace), (int64_t)B * Hkv * N * d, d, s);
   if (e != hipSuccess) return FP8ATTN_ELAUNCH;
   const bool pow2 = is_pow2(S);
   e = counts ? fp8attn::launch_fwd_count(p, d, pow2, s) : fp8attn::launch_fwd(p, d, pow2, s);

@@ -95,9 +95,9 @@ __device__ __forceinline__ unsigned bytes_below(int n) {
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
 // EXT: the options of fp8_attn_fwd_ex (sink split of block 0, quantized row sum); the
 // launches without them run the kernel compiled without their branches. QX: Q.K^T on the
-// bf16 matrix cores from the bf16 keys p.kx (d <= 128; two waves per SIMD).
+// bf16 matrix cores from the bf16 keys p.kx (d <= 128; three waves per SIMD).
 template <int D, bool POW2, bool OUT, bool CNT, bool EXT, bool QX>
-__global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) void fwd_kernel(const Params p) {
+__global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? (D <= 128 ? 3 : 2) : min_waves_per_simd(D)) void fwd_kernel(const Params p) {
   constexpr int kWaves = waves_for(D);
   constexpr int kThreads = 64 * kWaves;
   constexpr int kBlockM = kRowsPerWave * kWaves;
@@ -110,14 +110,11 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
   // staging: one LDS-DMA instruction moves 64 lanes x 16 bytes = 1 KiB of a tile
   constexpr int INST_PER_TILE = TILE / 1024;
   constexpr int RPW = (INST_PER_TILE + kWaves - 1) / kWaves;    // per wave and tile (at most)
-  // K rows: D bytes of E4M3, or 2 D bytes of bf16 (QX), in CHK 16-byte chunks. A bf16 row
-  // of d = 128 fills all 64 banks, so 16 consecutive rows read at one chunk need 16
-  // distinct slots: slot = chunk ^ (row & 15).
+  // K rows: D bytes of E4M3, or 2 D bytes of bf16 (QX, laid out in slices: below), in CHK
+  // 16-byte chunks
   static_assert(!QX || D <= 128, "the exact Q.K^T variant holds d <= 128");
   constexpr int KROW = QX ? 2 * D : D;
   constexpr int CHK = KROW / 16;
-  constexpr int SWZK = !QX ? SWZ : CHK >= 16 ? 15 : (CHK >= 8 ? 8 : CHK) - 1;
-  auto swzk = [](int j) { return SWZK == 15 ? (j & 15) : swz_row<SWZK>(j); };
   constexpr int TILE_K = kKvBlock * KROW;
   constexpr int INST_PER_TILE_K = TILE_K / 1024;
   constexpr int RPWK = (INST_PER_TILE_K + kWaves - 1) / kWaves;
@@ -193,16 +190,12 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
 #pragma unroll
     for (int e = 0; e < 2; ++e) koff[m][e] = col * D + (((4 * m + 2 * half + e) ^ swz(col)) << 4);
   auto kaddr = [&](int t, int m, int e) { return koff[m ^ (KT * t)][e] + 32 * t * D; };
-  // QX: the bf16 operand of instruction m for key row 32t + col: chunk 2m + half, slot
-  // (2m + half) ^ swzk(32t + col); with (j & 15) the slot does not depend on t
-  int koffx[QX ? 2 : 1][QX ? MX : 1];
-  if constexpr (QX) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int m = 0; m < MX; ++m)
-        koffx[t][m] = (32 * t + col) * KROW + (((2 * m + half) ^ swzk(32 * t + col)) << 4);
-  }
+  // QX: the bf16 keys of a block sit in MX slices of 2 KiB, slice m holding chunks 2m and
+  // 2m + 1 (d = 16m .. 16m + 15) of the 64 rows, 32 bytes a row; within a row the two
+  // chunks trade places on rows with bit 3 set. Sixteen lanes reading one chunk of 16
+  // consecutive rows then cover the 64 banks once, and the operand of instruction m for
+  // key row 32t + col is at a per-lane base plus the constant 2048 m + 1024 t.
+  const int kxoff = col * 32 + ((half ^ ((col >> 3) & 1)) << 4);
   // V^T operand through the transpose read: within a 16-lane group g, lane sl supplies key
   // row 16 tw + 8 (g >> 1) + (sl >> 1) and 8 columns of output tile u. Adding 16 tw to the
   // row flips swizzle bits 2 tw, i.e. tile u reads like tile u ^ tw.
@@ -231,8 +224,12 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
 #pragma unroll
   for (int r = 0; r < RPWK; ++r) {
     const int ii = wave + kWaves * r;
-    const int j = (1024 / KROW) * ii + lane / CHK, cs = lane % CHK;
-    goff[r] = j * KROW + ((cs ^ swzk(j)) << 4);
+    if constexpr (QX) {
+      goff[r] = 1024 * ii + 16 * (lane ^ ((lane >> 4) & 1));
+    } else {
+      const int j = (1024 / KROW) * ii + lane / CHK, cs = lane % CHK;
+      goff[r] = j * KROW + ((cs ^ swz(j)) << 4);
+    }
   }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -287,7 +284,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
         s[t] = f32x16{0};
 #pragma unroll
         for (int m = 0; m < MX; ++m)
-          s[t] = mfma_bf16(*(const i32x4*)(Ks + koffx[t][m]), qopx[m], s[t]);
+          s[t] = mfma_bf16(*(const i32x4*)(Ks + kxoff + 2048 * m + 1024 * t), qopx[m], s[t]);
       }
       return;
     }
@@ -333,7 +330,7 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
   };
   // the first NVPRE V operands are read before the softmax, so that their LDS latency is
   // spent under it
-  constexpr int NVPRE = D == 256 ? 0 : 1;   // d = 256 has no registers to spare
+  constexpr int NVPRE = (D == 256 || QX) ? 0 : 1;   // d = 256 and the bf16 Q.K^T have no registers to spare
   constexpr int NVARR = NVPRE > 0 ? NVPRE : 1;
 
   // ---- online softmax of block blk with scores s: running max and sum, the rescale of O,
@@ -572,14 +569,20 @@ __global__ FP8ATTN_BOUNDS(64 * waves_for(D), QX ? 2 : min_waves_per_simd(D)) voi
   }
 }
 
-// K (E4M3) -> the same values as bf16, 16 codes per thread.
-__global__ void keys_to_bf16_kernel(const uint8_t* __restrict__ k, uint8_t* __restrict__ kx, int64_t n16) {
+// K (E4M3) -> the same values as bf16, in the slice layout the exact Q.K^T kernel reads.
+// Thread t converts 16 codes: row R = 16 t / d of all heads' keys, d = e0 .. e0 + 15 with
+// e0 = 16 t % d, into 32 bytes at slice e0 / 16, row R % 64 of key block R / 64 (blocks
+// of 64 rows, 128 d bytes each; N is a multiple of 64, so no block spans two heads).
+__global__ void keys_to_bf16_kernel(const uint8_t* __restrict__ k, uint8_t* __restrict__ kx, int64_t n16, int d) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n16) return;
+  const int64_t R = 16 * t / d;
+  const int e0 = (int)(16 * t - R * d);
+  const int64_t out = (R / kKvBlock) * (int64_t)(kKvBlock * 2 * d) + 2048 * (e0 / 16) + 32 * (R % kKvBlock);
   const i32x4 w = ((const i32x4*)k)[t];
   const i32x2 a = e4m3x4_to_bf16x4(w.x), b = e4m3x4_to_bf16x4(w.y);
-  const i32x2 c = e4m3x4_to_bf16x4(w.z), d = e4m3x4_to_bf16x4(w.w);
-  ((i32x8*)kx)[t] = i32x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+  const i32x2 c = e4m3x4_to_bf16x4(w.z), e = e4m3x4_to_bf16x4(w.w);
+  *(i32x8*)(kx + out) = i32x8{a.x, a.y, b.x, b.y, c.x, c.y, e.x, e.y};
 }
 
 // Zero counts start at 0; the pair counts are known in closed form before the launch.
@@ -637,12 +640,12 @@ hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t strea
   return launch<true, false>(p, d, pow2_scale, stream);
 }
 
-hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, hipStream_t stream) {
+hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, int d, hipStream_t stream) {
   const int64_t n16 = n_elements / 16;
   if (n16 <= 0) return hipSuccess;
   const int64_t blocks = (n16 + 255) / 256;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(keys_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, kx, n16);
+  hipLaunchKernelGGL(keys_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, kx, n16, d);
   return hipGetLastError();
 }
 

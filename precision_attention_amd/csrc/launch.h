@@ -9,7 +9,8 @@ namespace fp8attn {
 struct Params {
   const uint8_t* q;                 // [B][H][N][d] E4M3
   const uint8_t* k;                 // [B][Hkv][N][d] E4M3
-  const uint8_t* kx;                // [B][Hkv][N][d] the same keys as bf16 (exact Q.K^T launches)
+  const uint8_t* kx;                // the same keys as bf16 (exact Q.K^T launches): per head and 64-key
+                                    // block, d / 16 slices [64 rows][d 16m .. 16m + 15]
   const uint8_t* v;                 // [B][Hkv][N][d] E4M3 (unused by a count-only launch)
   float* o;                         // [B][H][N][d] fp32 (unused by a count-only launch)
   const float* q_descale;           // [B*H]
@@ -67,8 +68,9 @@ struct DecodeParams {
 constexpr int decode_record_floats(int d) { return d + 4; }
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream);
-// K [B][Hkv][N][d] E4M3 -> kx, the same values as bf16 (exact), for the exact Q.K^T launches
-hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, hipStream_t stream);
+// K [B][Hkv][N][d] E4M3 -> kx, the same values as bf16 (exact) in the slice layout of
+// Params::kx, for the exact Q.K^T launches
+hipError_t launch_keys_to_bf16(const uint8_t* k, uint8_t* kx, int64_t n_elements, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
 hipError_t launch_fwd_count(const Params& p, int d, bool pow2_scale, hipStream_t stream);
