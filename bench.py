@@ -32,10 +32,18 @@ if ROOT not in sys.path:
 METRIC = "FP8 attn fwd TFLOP/s (causal, d=128) + %MFMA peak; P-collapse frac & MSE"
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 matrix peak (no sparsity)
 DEFAULT_WORKLOAD = "gqa_causal_h32_kv8_n32768_d128"
-KERNEL_SOURCES = ["precision_attention_amd/csrc/fwd.hip", "precision_attention_amd/csrc/launch.h",
+KERNEL_SOURCES = ["precision_attention_amd/csrc/fwd.hip", "precision_attention_amd/csrc/fwd16.hip",
+                  "precision_attention_amd/csrc/fwd_common.h", "precision_attention_amd/csrc/launch.h",
                   "precision_attention_amd/csrc/kernel_common.h"]
 DECODE_SOURCES = ["precision_attention_amd/csrc/decode.hip", "precision_attention_amd/csrc/launch.h",
                   "precision_attention_amd/csrc/kernel_common.h"]
+
+
+def fused_kernel_name(w) -> str:
+    """The fused forward + count kernel this workload launches (S = 256, reverse order)."""
+    from precision_attention_amd import binding
+    rows = binding.fwd_tile_rows(w.B, w.H, w.Hkv, w.N, w.d, causal=w.causal, kv_order="reverse", S=256.0)
+    return "fwd16_kernel<true, true, true>" if rows == 16 else f"fwd_kernel<{w.d}, true, true, true, false, false>"
 
 
 def log(msg):
@@ -247,7 +255,7 @@ def main():
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": flop / (ms_per_step * 1e-3) / 1e12, "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": flop / (ms_per_step * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                "traffic": traffic, "kernel": f"fwd_kernel<{w.d}, true, true, true, false, false>",
+                "traffic": traffic, "kernel": fused_kernel_name(w),
                 "flop_per_launch": flop}
 
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

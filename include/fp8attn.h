@@ -190,6 +190,20 @@ int fp8_attn_decode_static(const void* q, const void* k, const void* v, float* o
                            const float* q_descale, const float* k_descale, const float* v_descale,
                            int n_split, void* stream);
 
+/* Query rows per wave of the forward kernels (fp8_attn_fwd, _counted, _ex,
+ * _p_collapse_count, _exact_qk) for these arguments on the current device: 16 when d = 128,
+ * no fwd_ex option is in effect (kv_order is not FP8ATTN_KV_REVERSE_SINK_LAST with
+ * n_sink > 0, denominator is FP8ATTN_DENOM_FP32), exact_qk is 0, and the tiles of 128
+ * query rows, T = B * H * ceil(N / 128), are few: T <= 2 C with causal masking, 2 T <= C
+ * without (C: compute units of the device); else 32. Both shapes compute the same result:
+ * the 16-row kernel forms Q.K^T on the 16x16x128 FP8 matrix-core instruction, which
+ * accumulates like the 32x32x64 one, and P.V on the 16x16x32 one, in workgroups of 64
+ * rows, which fill and balance a small grid better. Returns 16 or 32,
+ * or a negative status for arguments the forward entry points would reject
+ * (EINVAL / EUNSUPPORTED as there). No GPU work; reads the device's compute-unit count. */
+int fp8_attn_fwd_tile_rows(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S,
+                           int n_sink, int denominator, int exact_qk);
+
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);
 

@@ -42,6 +42,8 @@ def _declare(lib):
     lib.fp8_attn_decode.restype = i
     lib.fp8_attn_decode_static.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp]
     lib.fp8_attn_decode_static.restype = i
+    lib.fp8_attn_fwd_tile_rows.argtypes = [i, i, i, i, i, i, i, f, i, i, i]
+    lib.fp8_attn_fwd_tile_rows.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -353,6 +355,17 @@ def decode_static(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str 
                                     int(n_split), _stream_ptr(dev, stream))
     _status(rc, "fp8_attn_decode_static")
     return out
+
+
+def fwd_tile_rows(B, H, Hkv, N, d, *, causal=True, kv_order="reverse", S=256.0, n_sink=4,
+                  denominator="fp32", exact_qk=False) -> int:
+    """Query rows per wave (16 or 32) the forward entry points use for these arguments on
+    the current device (fp8_attn_fwd_tile_rows)."""
+    rc = load().fp8_attn_fwd_tile_rows(B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                                       int(n_sink), DENOMINATORS[denominator], int(bool(exact_qk)))
+    if rc < 0:
+        _status(rc, "fp8_attn_fwd_tile_rows")
+    return rc
 
 
 def kv_block() -> int:

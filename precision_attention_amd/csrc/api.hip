@@ -8,6 +8,7 @@
 
 #include "fp8attn.h"
 #include "launch.h"
+#include "fwd_common.h"
 
 namespace {
 
@@ -316,6 +317,20 @@ int decode_impl(const void* q, const void* k, const void* v, float* o,
 }  // namespace
 
 extern "C" {
+
+int fp8_attn_fwd_tile_rows(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S,
+                           int n_sink, int denominator, int exact_qk) {
+  const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
+  if (st != FP8ATTN_OK) return st;
+  if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
+  if (denominator != FP8ATTN_DENOM_FP32 && denominator != FP8ATTN_DENOM_QUANTIZED) return FP8ATTN_EINVAL;
+  if (exact_qk != 0 && exact_qk != 1) return FP8ATTN_EINVAL;
+  if (exact_qk && d > 128) return FP8ATTN_EUNSUPPORTED;
+  fp8attn::Params p = make_params(nullptr, nullptr, nullptr, nullptr, B, H, Hkv, N, d, causal, kv_order, S,
+                                  nullptr, nullptr, nullptr, n_sink, nullptr, denominator);
+  p.exact_qk = exact_qk;
+  return fp8attn::fwd_tile_rows(p, d);
+}
 
 int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
 

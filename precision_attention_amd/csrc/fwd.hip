@@ -36,61 +36,15 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "launch.h"
 #include "kernel_common.h"
+#include "fwd_common.h"
 
 namespace fp8attn {
 namespace {
-
-// Map the linear workgroup id to (b, h, query tile). Workgroups are dispatched to the
-// 8 XCDs round-robin (id % 8); when the kv heads divide evenly, every XCD gets whole kv
-// heads (all their query heads), so K/V of one head stay in one XCD's L2, and within an
-// XCD the tiles run longest-first for causal masking. The order within an XCD is
-//  * rank-major (by default): tile rank r of every head of the XCD, then rank r + 1, so
-//    that the query heads sharing a kv head read the same K/V blocks at about the same time;
-//  * head-major (p.head_major: one query head per kv head and a head's K/V small enough
-//    for the XCD's 4 MB L2): all tiles of one head, then the next head, so that one head's
-//    K/V stays in L2 while its tiles run instead of many heads' K/V passing through it.
-__device__ __forceinline__ void map_tile(const Params& p, int ntiles, int& b, int& h, int& hk, int& qt) {
-  const int G = p.H / p.Hkv;
-  const int U = p.B * p.Hkv;
-  const int total = U * G * ntiles;
-  const int L = blockIdx.x;
-  int rank, unit, member;
-  if ((total & 7) == 0 && (U & 7) == 0) {
-    const int xcd = L & 7, slot = L >> 3;
-    const int upx = U >> 3;
-    if (p.head_major) {
-      const int uix = slot / ntiles;
-      rank = slot - uix * ntiles;
-      unit = xcd * upx + uix;
-      member = 0;
-    } else {
-      const int per_rank = upx * G;
-      rank = slot / per_rank;
-      const int rem = slot - rank * per_rank;
-      unit = xcd * upx + rem / G;
-      member = rem % G;
-    }
-  } else {
-    const int BH = p.B * p.H;
-    rank = L / BH;
-    const int bh = L - rank * BH;
-    unit = bh / G;
-    member = bh % G;
-  }
-  b = unit / p.Hkv;
-  hk = unit - b * p.Hkv;
-  h = hk * G + member;
-  qt = p.causal ? (ntiles - 1 - rank) : rank;
-}
-
-// Bit 7 of each of the first n bytes of a word (n clamped to 0 .. 4).
-__device__ __forceinline__ unsigned bytes_below(int n) {
-  return n >= 4 ? 0x80808080u : (n <= 0 ? 0u : (0x80808080u & ((1u << (8 * n)) - 1u)));
-}
 
 // OUT: compute and store O. CNT: count collapsed P casts (see fp8_attn_p_collapse_count).
 // EXT: the options of fp8_attn_fwd_ex (sink split of block 0, quantized row sum); the
@@ -625,6 +579,7 @@ hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.exact_qk && d > 128) return hipErrorInvalidValue;
+  if (fwd_tile_rows(p, d) == 16) return launch_fwd16(p, pow2, OUT, CNT, stream);
   switch (d) {
     case 64: launch_d<64, OUT, CNT>(p, pow2, stream); break;
     case 128: launch_d<128, OUT, CNT>(p, pow2, stream); break;
@@ -634,7 +589,32 @@ hipError_t launch(const Params& p, int d, bool pow2, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device, looked up once per device (0 if unknown).
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
+
+int fwd_tile_rows(const Params& p, int d) {
+  if (d != 128 || p.sink_last || p.qden || p.exact_qk) return 32;
+  // measured on MI355X (256 compute units): with causal masking, 64-row workgroups of
+  // 16-row waves balance the unequal tiles better up to two 128-row tiles per compute unit
+  // (9-21% faster); without it they win only while the 32-row grid leaves half the compute
+  // units idle (13-20%), and lose 2-5% at one tile per compute unit
+  const int cus = device_cu_count();
+  const int64_t tiles = num_workgroups(p, d);
+  return cus > 0 && (p.causal ? tiles <= 2ll * cus : 2 * tiles <= cus) ? 16 : 32;
+}
 
 hipError_t launch_fwd(const Params& p, int d, bool pow2_scale, hipStream_t stream) {
   return launch<true, false>(p, d, pow2_scale, stream);

@@ -22,6 +22,12 @@ int hw_probe_cvt_e4m3(const float* in, unsigned char* out, long n, void* stream)
 int hw_probe_mfma_dots(const unsigned char* a, const unsigned char* b, float* raw, int T, int kch,
                        void* stream);
 
+/* raw[t][i][j] = sum_c a[t][i][c] * b[t][j][c] over c < 128*kch, computed by kch chained
+ * v_mfma_f32_16x16x128_f8f6f4 with the k-slots of each instruction taken as the 128
+ * consecutive c values; a, b: [T][16][128*kch] E4M3 codes, raw: [T][16][16] fp32. */
+int hw_probe_mfma16_dots(const unsigned char* a, const unsigned char* b, float* raw, int T, int kch,
+                         void* stream);
+
 /* raw[t][i][j] = sum_c a[t][i][c] * b[t][j][c] over c < K (a multiple of 16), computed by
  * K/16 chained v_mfma_f32_32x32x16_bf16; a, b: [T][32][K] bf16 bit patterns (16-byte
  * aligned), raw: [T][32][32] fp32. */

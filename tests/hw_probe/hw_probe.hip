@@ -41,6 +41,27 @@ __global__ void mfma_kernel(const uint8_t* a, const uint8_t* b, float* raw, int 
   }
 }
 
+// 16x16x128 form: one wave per problem t; lane l feeds row l % 16, k-slots 32(l / 16) ..
+// +31 of each 128-wide chunk for both operands; the result layout is row 4(l / 16) + i,
+// col l % 16.
+__global__ void mfma16_kernel(const uint8_t* a, const uint8_t* b, float* raw, int kch) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int t = blockIdx.x, l = threadIdx.x;
+  const int K = 128 * kch;
+  const int r = l & 15, g = l >> 4;
+  f32x4 acc = {0};
+  for (int m = 0; m < kch; ++m) {
+    const uint8_t* pa = a + ((size_t)t * 16 + r) * K + 128 * m + 32 * g;
+    const uint8_t* pb = b + ((size_t)t * 16 + r) * K + 128 * m + 32 * g;
+    const i32x4 a0 = *(const i32x4*)pa, a1 = *(const i32x4*)(pa + 16);
+    const i32x4 b0 = *(const i32x4*)pb, b1 = *(const i32x4*)(pb + 16);
+    const i32x8 av = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const i32x8 bv = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+  }
+  for (int i = 0; i < 4; ++i) raw[((size_t)t * 16 + 4 * g + i) * 16 + r] = acc[i];
+}
+
 // bf16 form: one wave per problem t; a, b: [T][32][K] bf16 bits; k-slots 16m + 8h .. +7
 // of instruction m for lane half h; same result layout as mfma_kernel.
 __global__ void mfma_bf16_kernel(const uint16_t* a, const uint16_t* b, float* raw, int K) {
@@ -135,5 +156,13 @@ extern "C" int hw_probe_mfma_dots(const unsigned char* a, const unsigned char* b
   if (!a || !b || !raw || T <= 0 || kch <= 0 || kch > 64) return -1;
   if ((((uintptr_t)a) | ((uintptr_t)b)) & 15) return -1;
   hipLaunchKernelGGL(mfma_kernel, dim3(T), dim3(64), 0, (hipStream_t)stream, a, b, raw, kch);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hw_probe_mfma16_dots(const unsigned char* a, const unsigned char* b, float* raw, int T, int kch,
+                                    void* stream) {
+  if (!a || !b || !raw || T <= 0 || kch <= 0 || kch > 32) return -1;
+  if ((((uintptr_t)a) | ((uintptr_t)b)) & 15) return -1;
+  hipLaunchKernelGGL(mfma16_kernel, dim3(T), dim3(64), 0, (hipStream_t)stream, a, b, raw, kch);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

@@ -203,3 +203,22 @@ def test_decode_static_validation(lib):
     assert call(d=96) == -2
     assert call(B=8, H=64, Hkv=64, N=64 * 64, d=256, n_split=64) == -4
     assert lib.fp8_attn_status_string(-4).startswith(b"request exceeds")
+
+
+def _tile_rows(lib, B=1, H=8, Hkv=8, N=4096, d=128, causal=0, order=1, S=256.0, n_sink=4, den=0, exact=0):
+    return lib.fp8_attn_fwd_tile_rows(B, H, Hkv, N, d, causal, order, S, n_sink, den, exact)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), -1), (dict(H=3, Hkv=2), -1), (dict(causal=2), -1), (dict(order=3), -1), (dict(S=0.0), -1),
+    (dict(S=512.0), -1), (dict(n_sink=-1), -1), (dict(order=2, n_sink=65), -1), (dict(den=2), -1),
+    (dict(exact=2), -1), (dict(d=96), -2), (dict(N=100), -2), (dict(d=256, exact=1), -2),
+])
+def test_tile_rows_validation(lib, kw, status):
+    assert _tile_rows(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(d=64), dict(d=256), dict(order=2), dict(den=1), dict(exact=1)])
+def test_tile_rows_32_without_consulting_the_device(lib, kw):
+    # the 16-row kernel exists for d = 128 without the fwd_ex options or the exact Q.K^T only
+    assert _tile_rows(lib, **kw) == 32
