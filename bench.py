@@ -84,11 +84,19 @@ def measured_traffic(workload: str, kind: str = "fwd_counted"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def quality(inp, w, o_gpu, order, S, n_rows=64, heads=((0, 0), (0, 9), (0, 22), (0, 31))):
+def quality_heads(H):
+    """Heads of batch 0 sampled for the quality figures: 0, 9, 22 and 31 where they exist,
+    and the last head."""
+    return tuple((0, h) for h in sorted({h for h in (0, 9, 22, 31) if h < H} | {H - 1}))
+
+
+def quality(inp, w, o_gpu, order, S, n_rows=64, heads=None):
     """MSE of the GPU output against exact fp64 attention on the fp32 source tensors, and
     of a bf16 FlashAttention fed the same E4M3 operands (forward order, P rounded to bf16),
-    on sampled rows. Uses the oracle (CPU)."""
+    on sampled rows of ``quality_heads``. Uses the oracle (CPU)."""
     import numpy as np
+
+    heads = quality_heads(w.H) if heads is None else heads
 
     from oracle import attention as A
     from oracle import e4m3

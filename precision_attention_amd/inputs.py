@@ -68,6 +68,8 @@ WORKLOADS = {
                  descale="tensor", deltas=(0.0, 4.0, 6.0, 7.0, 8.0, 10.0, 12.0)),
         Workload("causal_b4_h32_n8192_d128", 4, 32, 32, 8192, 128, True, 8.0,
                  orders=("reverse", "forward"), scales=(256.0,), descale="head"),
+        Workload("causal_h4_n8192_d128", 1, 4, 4, 8192, 128, True, 8.0,
+                 orders=("reverse",), scales=(256.0,), descale="head"),
         Workload("gqa_causal_h32_kv8_n32768_d128", 1, 32, 8, 32768, 128, True, 10.0,
                  orders=("reverse", "forward"), scales=(256.0,), descale="head"),
         Workload("causal_h16_n65536_d128", 1, 16, 16, 65536, 128, True, 12.0,

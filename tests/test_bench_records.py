@@ -107,3 +107,13 @@ def test_committed_decode_traffic_records_are_consistent(wl):
     assert rec["hbm_over_algorithmic"] == pytest.approx((fetch + write) / w.bytes(), rel=1e-3)
     for cmd in rec["commands"]:
         assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
+
+
+def test_quality_heads_exist_for_every_workload():
+    import bench
+    from precision_attention_amd import inputs as I
+
+    for w in I.WORKLOADS.values():
+        heads = bench.quality_heads(w.H)
+        assert heads and all(b == 0 and 0 <= h < w.H for b, h in heads), w.name
+    assert bench.quality_heads(32) == ((0, 0), (0, 9), (0, 22), (0, 31))
