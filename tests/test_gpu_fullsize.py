@@ -128,6 +128,27 @@ def _check_mse_vs_bf16_fa(inp, w, o, heads, n_rows=64, limit=2.0):
     assert ratio <= limit
 
 
+def test_small_causal_h4_n8192_on_16_row_waves():
+    """The small causal workload (256 tiles of 128 rows), which the library runs on 16-row
+    waves on MI355X: sampled rows of two heads against the oracle, the pre-sink collapse,
+    and the counts of one whole head on both logit kinds."""
+    w = I.WORKLOADS["causal_h4_n8192_d128"]
+    rows16 = binding.fwd_tile_rows(w.B, w.H, w.Hkv, w.N, w.d, causal=True)
+    say(f"  {w.name}: {rows16}-row waves")
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 128:
+        assert rows16 == 16
+    inp, t, o, c = _run(w, "reverse", 256.0, heads=[(0, 0), (0, 3)], n_rows=320)
+    assert _presink_fraction_ok(c, w)
+    one = {k: v[0:1, 2:3].contiguous() for k, v in t.items()}
+    c1 = gpu_counts(one, causal=True, order="reverse", S=256.0)
+    sub = {k: v[0:1, 2:3] for k, v in inp.items()}
+    for logits in ("exact", "device"):
+        ref = oracle_attention.attention_e4m3(sub["q8"], sub["k8"], sub["v8"], sub["qd"], sub["kd"], sub["vd"],
+                                              causal=True, kv_order="reverse", S=256.0, logits=logits,
+                                              with_allowance=True, with_counts=True)
+        check_counts(c1, ref["counts"], ref["zero_flagged"], f"{w.name} head (0,2) [{logits} logits]")
+
+
 @pytest.mark.parametrize("name", ["causal_h16_n65536_d128", "causal_h16_n65536_d256"])
 def test_long_causal_n65536(name):
     w = I.WORKLOADS[name]
