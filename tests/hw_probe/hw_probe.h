@@ -46,6 +46,19 @@ int hw_probe_mfma_bf16_dots(const unsigned short* a, const unsigned short* b, fl
 int hw_probe_throughput(int kind, int blocks, int iters, const int* seed, float* sink, float* clock,
                         void* stream);
 
+/* Vector-ALU issue rate against occupancy. cus * waves_per_simd workgroups of 256 threads
+ * (one wave per SIMD each, so that on `cus` compute units every SIMD holds waves_per_simd
+ * waves; 1 <= waves_per_simd <= 8) run `iters` iterations of
+ *   pattern 0: 32 independent v_fma_f32;
+ *   pattern 1: 32 independent v_exp_f32;
+ *   pattern 2: the softmax core: 32 v_fma_f32 -> v_exp_f32, a pairwise row sum (32 v_add_f32)
+ *              and 16 v_cvt_pk_fp8_f32, plus 32 v_add_f32 that move the inputs.
+ * sink[blocks*256] receives one float per thread; cycles[w] and ticks[w] receive, for wave w
+ * (blocks*4 waves), the shader-clock ticks (s_memtime) and the 100 MHz real-time ticks
+ * (s_memrealtime) over its loop. seed: 256 ints. */
+int hw_probe_valu_rate(int pattern, int waves_per_simd, int cus, int iters, const int* seed, float* sink,
+                       unsigned long long* cycles, unsigned long long* ticks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

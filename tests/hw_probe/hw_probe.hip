@@ -125,6 +125,58 @@ __global__ __launch_bounds__(512) void throughput_kernel(int kind, int iters, co
   }
 }
 
+// Vector-ALU issue rate against occupancy: every wave runs `iters` iterations of one
+// pattern on 32 elements per lane; cycles[w] = shader-clock ticks (s_memtime) of wave w over
+// the loop, ticks[w] = 100 MHz real-time ticks over the same loop.
+template <int pattern>
+__global__ __launch_bounds__(256, 8) void valu_rate_kernel(int iters, const int* seed, float* sink,
+                                                        unsigned long long* cycles, unsigned long long* ticks,
+                                                        float a, float b) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = (float)(seed[(tid + 5 * i) & 255] & 1023) * 1e-4f;
+  unsigned w[4] = {};
+  float sum = 0.f;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (pattern == 0) {          // 32 independent v_fma_f32
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], a, b);
+    } else if constexpr (pattern == 1) {   // 32 independent v_exp_f32
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+    } else {                     // the softmax core: fma -> exp -> pairwise row sum, 16 E4M3 casts
+      float s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i], a, -b));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i + 1], a, -b));
+        s2 += p0 + p1;
+        w[i & 3] = (i >> 2) & 1 ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w[i & 3], true)
+                                : __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w[i & 3], false);
+      }
+      sum += s2;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = x[i] + 1e-7f;
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float r = sum;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r += x[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r += (float)w[i];
+  sink[(size_t)blockIdx.x * blockDim.x + tid] = r;
+  if (lane == 0) {
+    const size_t wv = (size_t)blockIdx.x * (blockDim.x >> 6) + (tid >> 6);
+    cycles[wv] = t1 - t0;
+    ticks[wv] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" int hw_probe_throughput(int kind, int blocks, int iters, const int* seed, float* sink, float* clock,
@@ -132,6 +184,24 @@ extern "C" int hw_probe_throughput(int kind, int blocks, int iters, const int* s
   if (kind < 0 || kind > 3 || blocks <= 0 || iters <= 0 || !seed || !sink || !clock) return -1;
   hipLaunchKernelGGL(throughput_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, kind, iters, seed,
                      sink, clock);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hw_probe_valu_rate(int pattern, int waves_per_simd, int cus, int iters, const int* seed, float* sink,
+                                  unsigned long long* cycles, unsigned long long* ticks, void* stream) {
+  if (pattern < 0 || pattern > 2 || waves_per_simd <= 0 || waves_per_simd > 8 || cus <= 0 || iters <= 0 || !seed ||
+      !sink || !cycles || !ticks)
+    return -1;
+  const dim3 grid(cus * waves_per_simd), block(256);
+  if (pattern == 0)
+    hipLaunchKernelGGL(valu_rate_kernel<0>, grid, block, 0, (hipStream_t)stream, iters, seed, sink, cycles, ticks,
+                       0.5f, 0.25f);
+  else if (pattern == 1)
+    hipLaunchKernelGGL(valu_rate_kernel<1>, grid, block, 0, (hipStream_t)stream, iters, seed, sink, cycles, ticks,
+                       0.5f, 0.25f);
+  else
+    hipLaunchKernelGGL(valu_rate_kernel<2>, grid, block, 0, (hipStream_t)stream, iters, seed, sink, cycles, ticks,
+                       0.5f, 0.25f);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
