@@ -277,6 +277,19 @@ def test_s256_beats_s448_forward(delta, lo, hi):
     assert lo < g < hi, g
 
 
+def test_s256_beats_s448_forward_over_seeds():
+    """The gain of one seed is a small-sample figure: every query row meets the same four
+    sink keys, so the sub-maximal sink P~, which dominate the output error, sit at the same
+    places in their E4M3 binade across rows (seed 0 gives the smallest gain of eight). Over
+    seeds 0-7 at Δ = 8 the gain is 4.4-9.6%, mean 7.5%; S = 256 wins on every seed."""
+    gains = []
+    for seed in range(8):
+        mse = _mse_pcast(4096, 8.0, [("forward", 256.0), ("forward", 448.0)], seed=seed)
+        gains.append(mse[("forward", 448.0)] / mse[("forward", 256.0)] - 1.0)
+    assert min(gains) > 0.03, gains
+    assert 0.06 < float(np.mean(gains)) < 0.09, gains
+
+
 def test_s448_step_excess_over_the_top_octave():
     """The d_p mechanism behind the printed 10-15% (technical summary, section 2
     "Optimization 2", condition 2; section 4, "Scale comparison"): for P~ spread over the
