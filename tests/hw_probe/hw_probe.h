@@ -34,6 +34,14 @@ int hw_probe_mfma16_dots(const unsigned char* a, const unsigned char* b, float* 
 int hw_probe_mfma_bf16_dots(const unsigned short* a, const unsigned short* b, float* raw, int T, int K,
                             void* stream);
 
+/* The older FP8 forms: raw[t][i][j] = sum_c a[t][i][c] * b[t][j][c] over c < K (a multiple
+ * of 32), computed by chained instructions with the k-slots of each instruction taken as
+ * consecutive c values. form 0: v_mfma_f32_32x32x16_fp8_fp8 (a, b: [T][32][K] E4M3 codes,
+ * raw: [T][32][32]); form 1: v_mfma_f32_16x16x32_fp8_fp8 (a, b: [T][16][K], raw:
+ * [T][16][16]). a, b 8-byte aligned. */
+int hw_probe_mfma_fp8_legacy_dots(int form, const unsigned char* a, const unsigned char* b, float* raw, int T,
+                                  int K, void* stream);
+
 /* Throughput kernel for the roofline denominators. Each of `blocks` workgroups of 512
  * threads (8 waves, 2 per SIMD) runs `iters` iterations of
  *   kind 0: 8 v_mfma_f32_32x32x64_f8f6f4 on 4 independent accumulators (131072 FLOP each);

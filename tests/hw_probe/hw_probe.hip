@@ -81,6 +81,38 @@ __global__ void mfma_bf16_kernel(const uint16_t* a, const uint16_t* b, float* ra
   }
 }
 
+// The older FP8 forms (CDNA3 instructions, kept on gfx950): one wave per problem t.
+// form 0: v_mfma_f32_32x32x16_fp8_fp8, lane l feeds row l % 32, k-slots 8(l / 32) .. +7 of
+//         each 16-wide chunk; result layout as mfma_kernel.
+// form 1: v_mfma_f32_16x16x32_fp8_fp8, lane l feeds row l % 16, k-slots 8(l / 16) .. +7 of
+//         each 32-wide chunk; result layout as mfma16_kernel.
+__global__ void mfma_fp8_legacy_kernel(int form, const uint8_t* a, const uint8_t* b, float* raw, int K) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int t = blockIdx.x, l = threadIdx.x;
+  if (form == 0) {
+    const int r = l & 31, h = l >> 5;
+    f32x16 acc = {0};
+    for (int m = 0; m < K / 16; ++m) {
+      const long av = *(const long*)(a + ((size_t)t * 32 + r) * K + 16 * m + 8 * h);
+      const long bv = *(const long*)(b + ((size_t)t * 32 + r) * K + 16 * m + 8 * h);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av, bv, acc, 0, 0, 0);
+    }
+    for (int q = 0; q < 16; ++q) {
+      const int row = 8 * (q >> 2) + 4 * h + (q & 3);
+      raw[((size_t)t * 32 + row) * 32 + r] = acc[q];
+    }
+  } else {
+    const int r = l & 15, g = l >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < K / 32; ++m) {
+      const long av = *(const long*)(a + ((size_t)t * 16 + r) * K + 32 * m + 8 * g);
+      const long bv = *(const long*)(b + ((size_t)t * 16 + r) * K + 32 * m + 8 * g);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, bv, acc, 0, 0, 0);
+    }
+    for (int i = 0; i < 4; ++i) raw[((size_t)t * 16 + 4 * g + i) * 16 + r] = acc[i];
+  }
+}
+
 __global__ __launch_bounds__(512) void throughput_kernel(int kind, int iters, const int* seed, float* sink,
                                                          float* clock) {
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -202,6 +234,14 @@ extern "C" int hw_probe_valu_rate(int pattern, int waves_per_simd, int cus, int 
   else
     hipLaunchKernelGGL(valu_rate_kernel<2>, grid, block, 0, (hipStream_t)stream, iters, seed, sink, cycles, ticks,
                        0.5f, 0.25f);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hw_probe_mfma_fp8_legacy_dots(int form, const unsigned char* a, const unsigned char* b, float* raw,
+                                            int T, int K, void* stream) {
+  if ((form != 0 && form != 1) || !a || !b || !raw || T <= 0 || K <= 0 || K % 32 || K > 4096) return -1;
+  if ((((uintptr_t)a) | ((uintptr_t)b)) & 7) return -1;
+  hipLaunchKernelGGL(mfma_fp8_legacy_kernel, dim3(T), dim3(64), 0, (hipStream_t)stream, form, a, b, raw, K);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

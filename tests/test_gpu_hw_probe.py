@@ -39,6 +39,7 @@ def probe():
     lib.hw_probe_mfma_bf16_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.hw_probe_mfma16_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.hw_probe_valu_rate.argtypes = [ctypes.c_int] * 4 + [vp] * 5
+    lib.hw_probe_mfma_fp8_legacy_dots.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     return lib
 
 
@@ -198,6 +199,33 @@ def test_hardware_bf16_mfma_is_exact_within_fp32_accumulation(probe, kind):
         f"{(np.abs(hw - exact) / bound).max():.3f}; median FP8-path bound / fp32 bound "
         f"{np.median(fp8_bound / bound):.0f}")
     assert (np.abs(hw - exact) <= bound).all()
+
+
+@pytest.mark.parametrize("form,rows", [(0, 32), (1, 16)])
+def test_older_fp8_mfma_forms_also_truncate(probe, form, rows):
+    """The two older FP8 forms gfx950 keeps (v_mfma_f32_32x32x16_fp8_fp8, form 0, and
+    v_mfma_f32_16x16x32_fp8_fp8, form 1), on sink-shaped dots of 64 slots: they too leave the
+    fp32-accumulation bound of exact products (so none of the FP8 forms forms Q.K^T exactly;
+    the exact variant uses the bf16 instruction), with errors of the size the 64-slot rule
+    bounds (printed: max |hw - exact| against both bounds)."""
+    T, K = 96, 64
+    rng = np.random.default_rng(90 + form)
+    a8, b8 = _operands(np.zeros((T, rows)), K, "sink", rng)
+    say(f"case hw older fp8 mfma form {form}")
+    dev = device()
+    ta = torch.from_numpy(np.ascontiguousarray(a8)).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(b8)).to(dev)
+    raw = torch.empty((T, rows, rows), dtype=torch.float32, device=dev)
+    assert probe.hw_probe_mfma_fp8_legacy_dots(form, ta.data_ptr(), tb.data_ptr(), raw.data_ptr(), T, K, None) == 0
+    torch.cuda.synchronize()
+    hw = raw.cpu().numpy().astype(np.float64)
+    exact = np.einsum("tik,tjk->tij", e4m3.decode(a8), e4m3.decode(b8))
+    fp32 = np.stack([mfma_model.fp32_accumulation_bound(a8[t], b8[t]) for t in range(T)])
+    rule = np.stack([mfma_model.error_bound(a8[t], b8[t]) for t in range(T)])
+    err = np.abs(hw - exact)
+    say(f"  max|hw-exact| {err.max():.3g}; dots beyond the fp32 bound {(err > fp32).mean():.4f}; "
+        f"max |hw-exact| / fp32 bound {(err / fp32).max():.1f}; / 64-slot rule bound {(err / rule).max():.3f}")
+    assert (err > fp32).any()
 
 
 def test_throughput_roofline_denominators(probe):
