@@ -46,7 +46,9 @@
  *    HIP error recorded right after the launch. Device-side faults (bad pointers) are
  *    reported by HIP on later calls, as for any kernel.
  *  - NaN codes (0x7F / 0xFF) or non-finite descales propagate NaN into O; not detected.
- *  - No global state, thread-safe, no exceptions cross the ABI.
+ *  - Thread-safe; no exceptions cross the ABI. The only global state is the static device
+ *    array of fp8_attn_decode_static (below) and a per-device cache of the compute-unit
+ *    count that fp8_attn_fwd_tile_rows reads.
  */
 #ifndef FP8ATTN_H
 #define FP8ATTN_H
@@ -195,9 +197,10 @@ int fp8_attn_decode_static(const void* q, const void* k, const void* v, float* o
  * no fwd_ex option is in effect (kv_order is not FP8ATTN_KV_REVERSE_SINK_LAST with
  * n_sink > 0, denominator is FP8ATTN_DENOM_FP32), exact_qk is 0, and the tiles of 128
  * query rows, T = B * H * ceil(N / 128), are few: T <= 2 C with causal masking, 2 T <= C
- * without (C: compute units of the device); else 32. Both shapes compute the same result:
- * the 16-row kernel forms Q.K^T on the 16x16x128 FP8 matrix-core instruction, which
- * accumulates like the 32x32x64 one, and P.V on the 16x16x32 one, in workgroups of 64
+ * without (C: compute units of the device); else 32. Both shapes compute the same method
+ * within the same parity tolerance: the 16-row kernel forms Q.K^T on the 16x16x128 FP8
+ * matrix-core instruction, which accumulates by the same rule as the 32x32x64 one, and P.V
+ * on the 16x16x32 one, whose own accumulation moves O by a few 1e-4, in workgroups of 64
  * rows, which fill and balance a small grid better. Returns 16 or 32,
  * or a negative status for arguments the forward entry points would reject
  * (EINVAL / EUNSUPPORTED as there). No GPU work; reads the device's compute-unit count. */
