@@ -18,8 +18,9 @@
 //   E4M3 cast, and O^T += V^T.P^T with V^T read by ds_read_b64_tr_b8, exactly as in the
 //   prefill kernel (fwd.hip). Every lane's row is its own query head, so the logit scale
 //   qd kd log2(e)/sqrt(d) is per lane.
-// * K and V blocks go HBM -> LDS by buffer_load ... lds into two buffers each; the wave
-//   waits only for its own DMA, so no barrier is needed.
+// * V blocks go HBM -> LDS by buffer_load ... lds into two buffers; K blocks (d <= 128) go
+//   straight to registers, one block ahead, with ordinary loads (at d = 256 K is staged
+//   through LDS like V). The wave waits only for its own loads, so no barrier is needed.
 // * The partial state of each (row, split) goes to the caller's workspace as a record of
 //   d + 4 floats, [acc[0..d), m (log2 units), l, 2 unused] (16-byte aligned records);
 //   decode_merge_kernel combines the splits.
@@ -34,15 +35,19 @@ namespace fp8attn {
 namespace {
 
 template <int D, bool POW2>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+__global__ FP8ATTN_BOUNDS(64, 2) void decode_kernel(const DecodeParams p) {
   constexpr int DM = D / 64;             // QK^T MFMAs per 32-key tile
   constexpr int DU = D / 32;             // 32-column output tiles
   constexpr int CH = D / 16;             // 16-byte chunks per row
   constexpr int SWZ = (CH >= 8 ? 8 : CH) - 1;
   constexpr int TILE = kKvBlock * D;     // bytes of one K or V block
   constexpr int RPW = TILE / 1024;       // DMA instructions per tile (one wave)
-  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  // d <= 128: K goes HBM -> registers, one block ahead (its MFMA operand is 32 contiguous
+  // bytes of a key row per lane), so that only V occupies LDS and more waves fit on a
+  // compute unit; d = 256 stages K through LDS as well (its operands would not fit)
+  constexpr bool KREG = D <= 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[KREG ? 16 : TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[KREG ? 16 : TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILE];
   auto swz = [](int j) { return swz_row<SWZ>(j); };
@@ -124,9 +129,24 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   auto dma_block = [&](int blk, lds_u8* kdst, lds_u8* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-      lds_dma16(Kg, p.N * D, kdst + q * 1024, goff[q], blk * TILE);
+      if (!KREG) lds_dma16(Kg, p.N * D, kdst + q * 1024, goff[q], blk * TILE);
       lds_dma16(Vg, p.N * D, vdst + q * 1024, goff[q], blk * TILE);
     }
+  };
+  // K operands of a block straight from HBM (KREG): operand (t, m) of lane (col, half) is
+  // key 32t + col, bytes 64m + 32 half .. + 32
+  typedef i32x8 kops_t[2][DM];
+  const uint8_t* const krow = Kg + (size_t)col * D + 32 * half;
+  auto load_k = [&](int blk, kops_t& ko) __attribute__((always_inline)) {
+    const uint8_t* base = krow + (size_t)blk * TILE;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < DM; ++m) {
+        const i32x4 lo = *(const i32x4*)(base + 32 * t * D + 64 * m);
+        const i32x4 hi = *(const i32x4*)(base + 32 * t * D + 64 * m + 16);
+        ko[t][m] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
   };
   auto block_of = [&](int n) { return p.reverse ? (blk1 - 1 - n) : (blk0 + n); };
 
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   for (int u = 0; u < DU; ++u) acc[u] = f32x16{0};
   const float bias_s = POW2 ? p.log2_S : 0.f;
 
-  auto step = [&](const uint8_t* Ks, const uint8_t* Vs) __attribute__((always_inline)) {
+  auto step = [&](const uint8_t* Ks, const uint8_t* Vs, const kops_t& kr) __attribute__((always_inline)) {
     // S^T = K . Q^T
     f32x16 s[2];
 #pragma unroll
@@ -145,9 +165,13 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
       s[t] = f32x16{0};
 #pragma unroll
       for (int m = 0; m < DM; ++m) {
-        const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
-        const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
-        s[t] = mfma_e4m3(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qop[m], s[t]);
+        if constexpr (KREG) {
+          s[t] = mfma_e4m3(kr[t][m], qop[m], s[t]);
+        } else {
+          const i32x4 lo = *(const i32x4*)(Ks + kaddr(t, m, 0));
+          const i32x4 hi = *(const i32x4*)(Ks + kaddr(t, m, 1));
+          s[t] = mfma_e4m3(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qop[m], s[t]);
+        }
       }
     }
     // running max of the row over the block (raw), then in log2 units
@@ -214,15 +238,24 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   lds_u8* const k1 = (lds_u8*)kb1;
   lds_u8* const v0 = (lds_u8*)vb0;
   lds_u8* const v1 = (lds_u8*)vb1;
+  // (KREG: K of block n in kr0 for even n, kr1 for odd n, loaded with V's DMA)
+  kops_t kr0, kr1;
   dma_block(block_of(0), k0, v0);
+  if constexpr (KREG) load_k(block_of(0), kr0);
   for (int n = 0; n < nb; n += 2) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): block n has landed
-    if (n + 1 < nb) dma_block(block_of(n + 1), k1, v1);
-    step(kb0, vb0);
+    if (n + 1 < nb) {
+      dma_block(block_of(n + 1), k1, v1);
+      if constexpr (KREG) load_k(block_of(n + 1), kr1);
+    }
+    step(kb0, vb0, kr0);
     if (n + 1 < nb) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
-      if (n + 2 < nb) dma_block(block_of(n + 2), k0, v0);
-      step(kb1, vb1);
+      if (n + 2 < nb) {
+        dma_block(block_of(n + 2), k0, v0);
+        if constexpr (KREG) load_k(block_of(n + 2), kr0);
+      }
+      step(kb1, vb1, kr1);
     }
   }
 
