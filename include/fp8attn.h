@@ -135,7 +135,7 @@ int fp8_attn_fwd_ex(const void* q, const void* k, const void* v, float* o,
  * small products inside its adder tree (up to ~2^-13 of the largest product of a group of
  * 8 k-slots); here S^T is formed on the bf16 matrix cores, which hold every E4M3 value
  * exactly, at half the FP8 rate. P.V stays on the FP8 matrix cores.
- *   d: 64 or 128 (EUNSUPPORTED otherwise).
+ *   d: 64 or 128, with 2*N*d <= 2^31-1 (one head's bf16 keys; EUNSUPPORTED otherwise).
  *   workspace: DEVICE buffer of at least fp8_attn_fwd_exact_qk_workspace_bytes(B, Hkv, N, d)
  *   bytes (the keys as bf16), 16-byte aligned, owned by the caller; its contents on entry do
  *   not matter and on return are unspecified. Calls sharing one workspace must not overlap.

@@ -185,6 +185,7 @@ int fp8_attn_fwd_exact_qk(const void* q, const void* k, const void* v, float* o,
   const int st = check_common(B, H, Hkv, N, d, causal, kv_order, S);
   if (st != FP8ATTN_OK) return st;
   if (d != 64 && d != 128) return FP8ATTN_EUNSUPPORTED;
+  if (2ll * N * d > INT32_MAX) return FP8ATTN_EUNSUPPORTED;   // one head's bf16 keys in a buffer range
   if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
   if (denominator != FP8ATTN_DENOM_FP32 && denominator != FP8ATTN_DENOM_QUANTIZED) return FP8ATTN_EINVAL;
   if (workspace_bytes < fp8_attn_fwd_exact_qk_workspace_bytes(B, Hkv, N, d)) return FP8ATTN_EINVAL;
@@ -325,7 +326,7 @@ int fp8_attn_fwd_tile_rows(int B, int H, int Hkv, int N, int d, int causal, int 
   if (!n_sink_ok(n_sink, N, kv_order)) return FP8ATTN_EINVAL;
   if (denominator != FP8ATTN_DENOM_FP32 && denominator != FP8ATTN_DENOM_QUANTIZED) return FP8ATTN_EINVAL;
   if (exact_qk != 0 && exact_qk != 1) return FP8ATTN_EINVAL;
-  if (exact_qk && d > 128) return FP8ATTN_EUNSUPPORTED;
+  if (exact_qk && (d > 128 || 2ll * N * d > INT32_MAX)) return FP8ATTN_EUNSUPPORTED;
   fp8attn::Params p = make_params(nullptr, nullptr, nullptr, nullptr, B, H, Hkv, N, d, causal, kv_order, S,
                                   nullptr, nullptr, nullptr, n_sink, nullptr, denominator);
   p.exact_qk = exact_qk;

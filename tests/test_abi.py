@@ -176,6 +176,9 @@ def test_binding_tensor_checks_on_cpu():
     (dict(ws=None), -1), (dict(ws_bytes=1), -1), (dict(d=256), -2), (dict(d=96), -2),
     (dict(order=3), -1), (dict(den=2), -1), (dict(n_sink=65, order=2), -1), (dict(ws=FAKE + 8), -2),
     (dict(S=449.0), -1), (dict(N=100), -2),
+    # one head's bf16 keys (2 N d bytes) must fit a 32-bit buffer range: N = 2^23 at d = 128
+    # is refused, N = 2^23 - 64 passes that check and fails on the small workspace
+    (dict(N=1 << 23), -2), (dict(N=(1 << 23) - 64), -1),
 ])
 def test_exact_qk_validation(lib, kw, status):
     a = dict(B=1, H=2, Hkv=1, N=128, d=128, causal=1, order=1, S=256.0, n_sink=4, den=0, ws=FAKE, ws_bytes=1 << 20)
@@ -213,6 +216,7 @@ def _tile_rows(lib, B=1, H=8, Hkv=8, N=4096, d=128, causal=0, order=1, S=256.0, 
     (dict(B=0), -1), (dict(H=3, Hkv=2), -1), (dict(causal=2), -1), (dict(order=3), -1), (dict(S=0.0), -1),
     (dict(S=512.0), -1), (dict(n_sink=-1), -1), (dict(order=2, n_sink=65), -1), (dict(den=2), -1),
     (dict(exact=2), -1), (dict(d=96), -2), (dict(N=100), -2), (dict(d=256, exact=1), -2),
+    (dict(N=1 << 23, d=128, exact=1), -2),
 ])
 def test_tile_rows_validation(lib, kw, status):
     assert _tile_rows(lib, **kw) == status
