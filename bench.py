@@ -70,9 +70,10 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kind: str = "fwd_counted"):
+def measured_traffic(workload: str, kind: str = "fwd_counted", n_split=None):
     """HBM bytes per launch (per call, for the decode's two kernels) from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel code (else None)."""
+    rocprofv3 counter summary, if it was taken on the current kernel code (and, for the
+    decode, at the same split count); else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -80,6 +81,8 @@ def measured_traffic(workload: str, kind: str = "fwd_counted"):
         rec = json.load(f)
     sources = DECODE_SOURCES if kind == "decode" else KERNEL_SOURCES
     if rec.get("kernel_source_hash") != kernel_source_hash(sources):
+        return None
+    if n_split is not None and rec.get("n_split") != n_split:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -352,7 +355,7 @@ def bench_decode(args, w):
                       "kv_order": args.order, "S": args.S, "n_split": n_split, "delta": w.delta,
                       "sink_construction": args.construction},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
-                        "traffic": measured_traffic(w.name, "decode"),
+                        "traffic": measured_traffic(w.name, "decode", n_split=n_split),
                         "kernel": "decode_kernel<128,pow2> + decode_merge_kernel",
                         "bytes_per_launch": nbytes},
            "tflops": w.flop() / (ms * 1e-3) / 1e12}

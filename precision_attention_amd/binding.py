@@ -274,14 +274,19 @@ def fwd_exact_qk(q8, k8, v8, q_descale, k_descale, v_descale, *, causal: bool, k
     return out, counts
 
 
-def decode_default_splits(B: int, Hkv: int, H: int, N: int, blocks_per_split: int = 32,
-                          min_waves: int = 256) -> int:
-    """Split count for fp8_attn_decode: about ``blocks_per_split`` 64-key blocks per split
-    (long enough to hide the DMA start-up and keep the merge small; measured best on MI355X
-    for 1-8 sequences of 32K-128K keys), but at least ``min_waves`` waves in the grid."""
+def decode_default_splits(B: int, Hkv: int, H: int, N: int, target_waves: int = 512,
+                          min_blocks_per_split: int = 8) -> int:
+    """Split count for fp8_attn_decode: enough splits for about ``target_waves`` waves in
+    the grid, two per compute unit of MI355X (one wave per (batch, KV head, group of up to 32
+    query heads, split)). Measured on MI355X for 1 sequence of 128K keys and 8 of 32K: one
+    wave per compute unit leaves the stream latency-bound (4.3-4.5 TB/s), four lose HBM
+    efficiency to the extra concurrent streams. Splits keep at least
+    ``min_blocks_per_split`` 64-key blocks where the sequence allows it, so that the per-split
+    start-up and the merge stay small."""
     nb = N // 64
     units = B * Hkv * ((H // Hkv + 31) // 32)
-    n = max(nb // blocks_per_split, -(-min_waves // units))
+    n = -(-target_waves // units)
+    n = min(n, max(1, nb // min_blocks_per_split))
     return max(1, min(nb, n))
 
 

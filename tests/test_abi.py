@@ -226,3 +226,16 @@ def test_tile_rows_validation(lib, kw, status):
 def test_tile_rows_32_without_consulting_the_device(lib, kw):
     # the 16-row kernel exists for d = 128 without the fwd_ex options or the exact Q.K^T only
     assert _tile_rows(lib, **kw) == 32
+
+
+def test_decode_default_splits_rule():
+    """About 512 waves (two per compute unit of MI355X), at least 8 blocks per split where N
+    allows, never more splits than blocks."""
+    from precision_attention_amd import binding
+
+    assert binding.decode_default_splits(1, 8, 32, 131072) == 64      # 8 units x 64 = 512 waves
+    assert binding.decode_default_splits(8, 8, 32, 32768) == 8        # 64 units x 8
+    assert binding.decode_default_splits(1, 8, 32, 4096) == 8         # 64 blocks: 8 per split
+    assert binding.decode_default_splits(1, 1, 1, 64) == 1            # one block
+    assert binding.decode_default_splits(64, 8, 8, 32768) == 1        # 512 units need no split
+    assert binding.decode_default_splits(1, 2, 80, 65536) == 128      # 2 KV heads x 3 query groups

@@ -107,6 +107,19 @@ def test_committed_decode_traffic_records_are_consistent(wl):
     assert rec["hbm_over_algorithmic"] == pytest.approx((fetch + write) / w.bytes(), rel=1e-3)
     for cmd in rec["commands"]:
         assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
+    # taken at the split count the bench runs
+    from precision_attention_amd import binding
+
+    assert rec["n_split"] == binding.decode_default_splits(w.B, w.Hkv, w.H, w.N)
+
+
+def test_decode_record_follows_the_split_count(tmp_path, monkeypatch):
+    wl = "decode_b8_gqa_h32_kv8_n32768_d128"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "abc")
+    _write(tmp_path, f"traffic_decode_{wl}.json", {"kernel_source_hash": "abc", "n_split": 8, "hbm_bytes_per_launch": 7})
+    assert bench.measured_traffic(wl, "decode", n_split=8) == 7
+    assert bench.measured_traffic(wl, "decode", n_split=16) is None
 
 
 def test_quality_heads_exist_for_every_workload():
