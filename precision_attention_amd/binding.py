@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfp8attn.so")
 
 FP8ATTN_OK = 0
+STATIC_SCRATCH_BYTES = 8 << 20    # FP8ATTN_STATIC_SCRATCH_BYTES of include/fp8attn.h
 KV_ORDERS = {"forward": 0, "reverse": 1, "reverse_sink_last": 2}
 DENOMINATORS = {"fp32": 0, "quantized": 1}
 
@@ -332,7 +333,8 @@ def decode(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reve
 def decode_static(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str = "reverse", S: float = 256.0,
                   n_split: int | None = None, out=None, stream=None):
     """``decode`` with the split records in the library's static per-GPU scratch
-    (fp8_attn_decode_static: no workspace; calls overlapping on one GPU race)."""
+    (fp8_attn_decode_static: no workspace; calls overlapping on one GPU race). Without
+    ``n_split``, the default split count is lowered to what the scratch holds."""
     import torch
 
     lib = load()
@@ -351,7 +353,9 @@ def decode_static(q8, k8, v8, q_descale, k_descale, v_descale, *, kv_order: str 
     kd = _as_descale(k_descale, B * Hkv, "k_descale", dev)
     vd = _as_descale(v_descale, B * Hkv, "v_descale", dev)
     if n_split is None:
-        n_split = decode_default_splits(B, Hkv, H, N)
+        per_split = lib.fp8_attn_decode_workspace_bytes(B, H, d, 1)
+        fit = STATIC_SCRATCH_BYTES // per_split if per_split else 1
+        n_split = max(1, min(decode_default_splits(B, Hkv, H, N), fit))
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     _check_tensor(out, "out", dev, torch.float32, shape=(B, H, d))

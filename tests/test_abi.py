@@ -239,3 +239,11 @@ def test_decode_default_splits_rule():
     assert binding.decode_default_splits(1, 1, 1, 64) == 1            # one block
     assert binding.decode_default_splits(64, 8, 8, 32768) == 1        # 512 units need no split
     assert binding.decode_default_splits(1, 2, 80, 65536) == 128      # 2 KV heads x 3 query groups
+
+
+def test_binding_static_scratch_size_matches_the_header():
+    from precision_attention_amd import binding
+
+    with open(os.path.join(ROOT, "include", "fp8attn.h")) as f:
+        m = re.search(r"#define FP8ATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and binding.STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))

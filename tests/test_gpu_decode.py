@@ -118,3 +118,22 @@ def test_decode_deterministic_and_workspace_reuse():
     b = binding.decode(t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"], n_split=16, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_decode_static_default_splits_fit_the_scratch():
+    """Without n_split, decode_static lowers the default split count to what the static
+    scratch holds: one KV head of N = 262144 keys with 32 query heads gets 512 splits by
+    default (8.6 MB of records), and the 8 MiB scratch holds 496. The result is bitwise equal
+    to the workspace decode at 496 splits."""
+    B, H, Hkv, N, d = 1, 32, 1, 262144, 128
+    assert binding.decode_default_splits(B, Hkv, H, N) == 512
+    fit = binding.STATIC_SCRATCH_BYTES // binding.load().fp8_attn_decode_workspace_bytes(B, H, d, 1)
+    assert fit == 496
+    inp = _decode_inputs(B, H, Hkv, N, d, 10.0, seed=77)
+    t = to_device(inp)
+    say(f"case static-scratch decode B{B} H{H} Hkv{Hkv} N{N} d{d}, default splits")
+    args = (t["q8"], t["k8"], t["v8"], t["qd"], t["kd"], t["vd"])
+    got = binding.decode_static(*args, kv_order="reverse", S=256.0)
+    ref = binding.decode(*args, kv_order="reverse", S=256.0, n_split=fit)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
