@@ -4,7 +4,10 @@ fp8_attn_fwd_ex and fp8_attn_fwd_exact_qk; batch, head grouping, every head size
 query tiles, both masks, the three block orders, S powers of two and not, sink strength,
 both sink constructions, n_sink and both denominators. Every case is checked against the
 exact-logit oracle (with the allowance its Q.K^T accumulation implies) and the counts
-against the oracle's and the closed-form pair totals."""
+against the oracle's and the closed-form pair totals. FP8ATTN_SWEEP_CASES and
+FP8ATTN_SWEEP_SEED widen or reseed the sweep (default: 24 cases, seed 4242)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -40,7 +43,9 @@ def _cases(n=24, seed=4242):
     return out
 
 
-@pytest.mark.parametrize("entry,B,H,Hkv,N,d,causal,order,S,delta,construction,n_sink,denominator", _cases())
+@pytest.mark.parametrize("entry,B,H,Hkv,N,d,causal,order,S,delta,construction,n_sink,denominator",
+                         _cases(n=int(os.environ.get("FP8ATTN_SWEEP_CASES", "24")),
+                                seed=int(os.environ.get("FP8ATTN_SWEEP_SEED", "4242"))))
 def test_random_sweep(entry, B, H, Hkv, N, d, causal, order, S, delta, construction, n_sink, denominator):
     inp = I.make_inputs(B, H, Hkv, N, d, delta=delta, seed=13 * N + d + B + H, descale="head",
                         construction=construction)
