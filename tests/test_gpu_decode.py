@@ -4,6 +4,8 @@ every query over all N keys, the split partition reproduced by
 the oracle. Same two references as the prefill parity tests: the exact-logit oracle with
 the analytic logit-interval allowance, and the oracle on the matrix core's own logits with
 only the rounding-boundary allowance."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -73,7 +75,8 @@ def test_decode_parity(B, H, Hkv, N, d, order, S, delta, n_split):
 
 def _random_cases(n=10, seed=31):
     """Seeded random decode shapes: query groups from 1 to 40 heads per KV head, split
-    counts from 1 to every block, both orders, S powers of two and not."""
+    counts from 1 to every block, both orders, S powers of two and not.
+    FP8ATTN_DECODE_CASES and FP8ATTN_DECODE_SEED widen or reseed them (default 10, 31)."""
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
@@ -89,7 +92,9 @@ def _random_cases(n=10, seed=31):
     return out
 
 
-@pytest.mark.parametrize("B,H,Hkv,N,d,order,S,delta,n_split", _random_cases())
+@pytest.mark.parametrize("B,H,Hkv,N,d,order,S,delta,n_split",
+                         _random_cases(n=int(os.environ.get("FP8ATTN_DECODE_CASES", "10")),
+                                       seed=int(os.environ.get("FP8ATTN_DECODE_SEED", "31"))))
 def test_decode_random_parity(B, H, Hkv, N, d, order, S, delta, n_split):
     test_decode_parity(B, H, Hkv, N, d, order, S, delta, n_split)
 
