@@ -42,6 +42,12 @@ int hw_probe_mfma_bf16_dots(const unsigned short* a, const unsigned short* b, fl
 int hw_probe_mfma_fp8_legacy_dots(int form, const unsigned char* a, const unsigned char* b, float* raw, int T,
                                   int K, void* stream);
 
+/* Streaming read of `bytes` (a multiple of 16) at `in` (16-byte aligned): `blocks`
+ * workgroups of 256 threads read the buffer once in 16-byte words at a grid stride, eight
+ * loads in flight per thread, and out[blocks*256] receives each thread's XOR of its words
+ * (so no load is dead code; the XOR of all of out is the XOR of the buffer's 32-bit words). */
+int hw_probe_stream_read(const void* in, long bytes, int blocks, int* out, void* stream);
+
 /* Throughput kernel for the roofline denominators. Each of `blocks` workgroups of 512
  * threads (8 waves, 2 per SIMD) runs `iters` iterations of
  *   kind 0: 8 v_mfma_f32_32x32x64_f8f6f4 on 4 independent accumulators (131072 FLOP each);

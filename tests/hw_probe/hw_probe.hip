@@ -209,7 +209,32 @@ __global__ __launch_bounds__(256, 8) void valu_rate_kernel(int iters, const int*
   }
 }
 
+// Streaming read: thread t reads the 16-byte words t, t + S, t + 2S, ... (S = all threads)
+// and XORs them, eight loads in flight per step; out[t] = the XOR of its four lanes.
+__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* __restrict__ in, long n16, int* out) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  i32x4 acc = {0, 0, 0, 0};
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    i32x4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(in + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= w[u];
+  }
+  for (; i < n16; i += stride) acc ^= in[i];
+  out[(long)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
+
+extern "C" int hw_probe_stream_read(const void* in, long bytes, int blocks, int* out, void* stream) {
+  if (!in || !out || bytes <= 0 || bytes % 16 != 0 || blocks <= 0 || (reinterpret_cast<uintptr_t>(in) & 15) != 0)
+    return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const i32x4*>(in), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int hw_probe_throughput(int kind, int blocks, int iters, const int* seed, float* sink, float* clock,
                                    void* stream) {

@@ -40,6 +40,7 @@ def probe():
     lib.hw_probe_mfma16_dots.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.hw_probe_valu_rate.argtypes = [ctypes.c_int] * 4 + [vp] * 5
     lib.hw_probe_mfma_fp8_legacy_dots.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.hw_probe_stream_read.argtypes = [vp, ctypes.c_long, ctypes.c_int, vp, vp]
     return lib
 
 
@@ -307,3 +308,48 @@ def test_valu_throughput_against_occupancy(probe):
     assert soft[2][0] >= 0.85 * soft[0][0]
     assert 3.5 < table["32 v_fma_f32"][7][0] / 32 < 5.0
     assert 7.0 < table["32 v_exp_f32"][7][0] / 32 < 10.0
+
+
+def test_stream_read_bandwidth(probe):
+    """The practical HBM read bandwidth, the ceiling of the split-KV decode's stream: a 4 GiB
+    buffer read once in 16-byte words at a grid stride (eight loads in flight per thread) by
+    grids of 1 to 32 workgroups per compute unit, event-timed, best of five launches each. The
+    device-to-device copy of 1 GiB (read + write) is printed beside it. The XOR the kernel
+    returns is checked on a small buffer first, so the timed reads are real."""
+    dev = device()
+    stream = torch.cuda.current_stream(dev)
+    s = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    small = np.random.default_rng(5).integers(0, 2**31 - 1, 1 << 20).astype(np.int32)
+    buf = torch.from_numpy(small).to(dev)
+    out = torch.empty(4 * cus * 256, dtype=torch.int32, device=dev)
+    assert probe.hw_probe_stream_read(buf.data_ptr(), buf.numel() * 4, 4 * cus, out.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(out.cpu().numpy()) == np.bitwise_xor.reduce(small)
+    nbytes = 4 << 30
+    big = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    rows = []
+    for per_cu in (1, 2, 4, 8, 16, 32):
+        blocks = per_cu * cus
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert probe.hw_probe_stream_read(big.data_ptr(), nbytes, blocks, out.data_ptr(), s) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        rows.append((per_cu, nbytes / best / 1e9))
+    say("  stream read, 4 GiB: " + "  ".join(f"{p} WG/CU {g:.0f} GB/s" for p, g in rows))
+    src, dst = big[: 1 << 30], torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    say(f"  device-to-device copy, 1 GiB: {2 * (1 << 30) / best / 1e9:.0f} GB/s (read + write)")
+    assert max(g for _, g in rows) > 4000
