@@ -41,7 +41,10 @@ DECODE_SOURCES = ["precision_attention_amd/csrc/decode.hip", "precision_attentio
 def fused_kernel_name(w) -> str:
     """The fused forward + count kernel this workload launches (S = 256, reverse order)."""
     from precision_attention_amd import binding
-    rows = binding.fwd_tile_rows(w.B, w.H, w.Hkv, w.N, w.d, causal=w.causal, kv_order="reverse", S=256.0)
+    kw = dict(causal=w.causal, kv_order="reverse", S=256.0)
+    if binding.fwd_walk_groups(w.B, w.H, w.Hkv, w.N, w.d, **kw) == 2:
+        return "fwd_pair_kernel<true, true, true>"
+    rows = binding.fwd_tile_rows(w.B, w.H, w.Hkv, w.N, w.d, **kw)
     return "fwd16_kernel<true, true, true>" if rows == 16 else f"fwd_kernel<{w.d}, true, true, true, false, false>"
 
 

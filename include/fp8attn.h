@@ -48,7 +48,7 @@
  *  - NaN codes (0x7F / 0xFF) or non-finite descales propagate NaN into O; not detected.
  *  - Thread-safe; no exceptions cross the ABI. The only global state is the static device
  *    array of fp8_attn_decode_static (below) and a per-device cache of the compute-unit
- *    count that fp8_attn_fwd_tile_rows reads.
+ *    count that fp8_attn_fwd_tile_rows and fp8_attn_fwd_walk_groups read.
  */
 #ifndef FP8ATTN_H
 #define FP8ATTN_H
@@ -193,19 +193,39 @@ int fp8_attn_decode_static(const void* q, const void* k, const void* v, float* o
                            int n_split, void* stream);
 
 /* Query rows per wave of the forward kernels (fp8_attn_fwd, _counted, _ex,
- * _p_collapse_count, _exact_qk) for these arguments on the current device: 16 when d = 128,
- * no fwd_ex option is in effect (kv_order is not FP8ATTN_KV_REVERSE_SINK_LAST with
- * n_sink > 0, denominator is FP8ATTN_DENOM_FP32), exact_qk is 0, and the tiles of 128
- * query rows, T = B * H * ceil(N / 128), are few: T <= 2 C with causal masking, 2 T <= C
- * without (C: compute units of the device); else 32. Both shapes compute the same method
- * within the same parity tolerance: the 16-row kernel forms Q.K^T on the 16x16x128 FP8
- * matrix-core instruction, which accumulates by the same rule as the 32x32x64 one, and P.V
- * on the 16x16x32 one, whose own accumulation moves O by a few 1e-4, in workgroups of 64
- * rows, which fill and balance a small grid better. Returns 16 or 32,
- * or a negative status for arguments the forward entry points would reject
- * (EINVAL / EUNSUPPORTED as there). No GPU work; reads the device's compute-unit count. */
+ * _p_collapse_count, _exact_qk) for these arguments on the current device. Let C be the
+ * device's compute units and T = B * H * ceil(N / 128) the tiles of 128 query rows. The
+ * result is 16 when all of these hold, else 32:
+ *  - d = 128;
+ *  - no fwd_ex option is in effect: kv_order is not FP8ATTN_KV_REVERSE_SINK_LAST with
+ *    n_sink > 0, and denominator is FP8ATTN_DENOM_FP32;
+ *  - exact_qk is 0;
+ *  - the forward has causal masking and 1.5 C < T <= 2 C. Below that the walk groups of
+ *    fp8_attn_fwd_walk_groups take the grid.
+ * Both shapes compute the same method within the same parity tolerance. The 16-row kernel
+ * forms Q.K^T on the 16x16x128 FP8 matrix-core instruction, which accumulates by the same
+ * rule as the 32x32x64 one. It forms P.V on the 16x16x32 one, whose own accumulation moves
+ * O by a few 1e-4. Its workgroups of 64 rows fill and balance such a grid better.
+ * Returns 16 or 32, or the negative status (EINVAL / EUNSUPPORTED) that the forward entry
+ * points would return for these arguments. No GPU work; reads the device's compute-unit
+ * count. */
 int fp8_attn_fwd_tile_rows(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S,
                            int n_sink, int denominator, int exact_qk);
+
+/* Walk groups of the 32-row forward kernel for these arguments on the current device (same
+ * arguments and statuses as fp8_attn_fwd_tile_rows; C and T as there). The result is 2 when
+ * d = 128, no fwd_ex option is in effect, exact_qk is 0, and the grid is small: 2 T <= 3 C
+ * with causal masking, 2 T <= C without. Else it is 1.
+ * With 2, a workgroup of 4 waves takes 64 query rows, and two groups of 2 waves split the
+ * walk over the KV blocks: group g visits the walk positions g, g + 2, g + 4, ... After each
+ * block's Q.K^T the groups trade their block row maxima through LDS. Each block's running
+ * maximum, and so every P~ and its E4M3 code, is then the one of the sequential walk
+ * ("P-Cast Precision in FP8 Attention", technical summary section 1: the running max
+ * updated per KV block in the visiting order). The two partial states are merged once at
+ * the end, which changes only the fp32 summation order of O. Counts are the same as with 1.
+ * No GPU work; reads the device's compute-unit count. */
+int fp8_attn_fwd_walk_groups(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S,
+                             int n_sink, int denominator, int exact_qk);
 
 /* Width in keys of the KV blocks between running-max updates (64). */
 int fp8_attn_kv_block(void);

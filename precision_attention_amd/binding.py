@@ -45,6 +45,8 @@ def _declare(lib):
     lib.fp8_attn_decode_static.restype = i
     lib.fp8_attn_fwd_tile_rows.argtypes = [i, i, i, i, i, i, i, f, i, i, i]
     lib.fp8_attn_fwd_tile_rows.restype = i
+    lib.fp8_attn_fwd_walk_groups.argtypes = [i, i, i, i, i, i, i, f, i, i, i]
+    lib.fp8_attn_fwd_walk_groups.restype = i
     lib.fp8_attn_kv_block.argtypes = []
     lib.fp8_attn_kv_block.restype = i
     lib.fp8_attn_version.argtypes = []
@@ -374,6 +376,18 @@ def fwd_tile_rows(B, H, Hkv, N, d, *, causal=True, kv_order="reverse", S=256.0, 
                                        int(n_sink), DENOMINATORS[denominator], int(bool(exact_qk)))
     if rc < 0:
         _status(rc, "fp8_attn_fwd_tile_rows")
+    return rc
+
+
+def fwd_walk_groups(B, H, Hkv, N, d, *, causal=True, kv_order="reverse", S=256.0, n_sink=4,
+                    denominator="fp32", exact_qk=False) -> int:
+    """Walk groups (1, or 2: 64-row tiles whose KV walk two groups of waves split) the
+    32-row forward uses for these arguments on the current device
+    (fp8_attn_fwd_walk_groups)."""
+    rc = load().fp8_attn_fwd_walk_groups(B, H, Hkv, N, d, int(bool(causal)), KV_ORDERS[kv_order], float(S),
+                                         int(n_sink), DENOMINATORS[denominator], int(bool(exact_qk)))
+    if rc < 0:
+        _status(rc, "fp8_attn_fwd_walk_groups")
     return rc
 
 

@@ -333,6 +333,16 @@ int fp8_attn_fwd_tile_rows(int B, int H, int Hkv, int N, int d, int causal, int 
   return fp8attn::fwd_tile_rows(p, d);
 }
 
+int fp8_attn_fwd_walk_groups(int B, int H, int Hkv, int N, int d, int causal, int kv_order, float S,
+                             int n_sink, int denominator, int exact_qk) {
+  const int rows = fp8_attn_fwd_tile_rows(B, H, Hkv, N, d, causal, kv_order, S, n_sink, denominator, exact_qk);
+  if (rows < 0) return rows;
+  fp8attn::Params p = make_params(nullptr, nullptr, nullptr, nullptr, B, H, Hkv, N, d, causal, kv_order, S,
+                                  nullptr, nullptr, nullptr, n_sink, nullptr, denominator);
+  p.exact_qk = exact_qk;
+  return fp8attn::fwd_walk_groups(p, d);
+}
+
 int fp8_attn_kv_block(void) { return fp8attn::kKvBlock; }
 
 const char* fp8_attn_version(void) { return "fp8attn-gfx950 0.2.0"; }

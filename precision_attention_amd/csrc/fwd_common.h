@@ -66,6 +66,9 @@ __device__ __forceinline__ unsigned bytes_below(int n) {
 // at most two per compute unit of the current device (causal) or at most one per two
 // compute units (not causal), else 32.
 int fwd_tile_rows(const Params& p, int d);
+// Walk groups of the 32-row forward launch: 2 when 64-row tiles are walked by two groups
+// of two waves (d = 128 without the fwd_ex options or the exact Q.K^T), else 1.
+int fwd_walk_groups(const Params& p, int d);
 // The 16-row forward (d = 128); the caller has set the counts if `count`.
 hipError_t launch_fwd16(const Params& p, bool pow2, bool out, bool count, hipStream_t stream);
 

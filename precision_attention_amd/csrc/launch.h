@@ -37,6 +37,8 @@ constexpr int kRowsPerWave = 32;
 constexpr int kKvBlock = 64;
 
 constexpr int waves_for(int) { return 4; }
+// waves per walk group of the two-group forward (64-row tiles)
+constexpr int kPairWaves = 2;
 // Register budget: at most 512 / n VGPRs per lane lets n waves share a SIMD.
 constexpr int min_waves_per_simd(int d) { return d == 256 ? 2 : 3; }
 constexpr int block_m_for(int d) { return kRowsPerWave * waves_for(d); }

@@ -228,6 +228,27 @@ def test_tile_rows_32_without_consulting_the_device(lib, kw):
     assert _tile_rows(lib, **kw) == 32
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), -1), (dict(H=3, Hkv=2), -1), (dict(causal=2), -1), (dict(order=3), -1), (dict(S=0.0), -1),
+    (dict(S=512.0), -1), (dict(n_sink=-1), -1), (dict(order=2, n_sink=65), -1), (dict(den=2), -1),
+    (dict(exact=2), -1), (dict(d=96), -2), (dict(N=100), -2), (dict(d=256, exact=1), -2),
+    (dict(N=1 << 23, d=128, exact=1), -2),
+])
+def test_walk_groups_validation(lib, kw, status):
+    # the same checks, and so the same statuses, as the tile-rows query
+    assert _walk_groups(lib, **kw) == status == _tile_rows(lib, **kw)
+
+
+@pytest.mark.parametrize("kw", [dict(d=64), dict(d=256), dict(order=2), dict(den=1), dict(exact=1)])
+def test_walk_groups_1_without_consulting_the_device(lib, kw):
+    # the two-group walk exists for d = 128 without the fwd_ex options or the exact Q.K^T only
+    assert _walk_groups(lib, **kw) == 1
+
+
+def _walk_groups(lib, B=1, H=8, Hkv=8, N=4096, d=128, causal=0, order=1, S=256.0, n_sink=4, den=0, exact=0):
+    return lib.fp8_attn_fwd_walk_groups(B, H, Hkv, N, d, causal, order, S, n_sink, den, exact)
+
+
 def test_decode_default_splits_rule():
     """About 512 waves (two per compute unit of MI355X), at least 8 blocks per split where N
     allows, never more splits than blocks."""

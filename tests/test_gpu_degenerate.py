@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [
     # B, H, Hkv, N, d, causal, order
-    (1, 2, 1, 448, 128, True, "reverse"),      # small causal grid: 16-row waves
+    (1, 2, 1, 448, 128, True, "reverse"),      # small causal grid: two walk groups
     (1, 2, 2, 320, 64, False, "forward"),      # d = 64: 32-row waves
     (2, 4, 2, 256, 128, False, "reverse"),
 ]

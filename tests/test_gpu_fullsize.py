@@ -128,15 +128,15 @@ def _check_mse_vs_bf16_fa(inp, w, o, heads, n_rows=64, limit=2.0):
     assert ratio <= limit
 
 
-def test_small_causal_h4_n8192_on_16_row_waves():
-    """The small causal workload (256 tiles of 128 rows), which the library runs on 16-row
-    waves on MI355X: sampled rows of two heads against the oracle, the pre-sink collapse,
-    and the counts of one whole head on both logit kinds."""
+def test_small_causal_h4_n8192_on_walk_groups():
+    """The small causal workload (256 tiles of 128 rows), which the library runs as 64-row
+    tiles walked by two groups of waves on MI355X: sampled rows of two heads against the
+    oracle, the pre-sink collapse, and the counts of one whole head on both logit kinds."""
     w = I.WORKLOADS["causal_h4_n8192_d128"]
-    rows16 = binding.fwd_tile_rows(w.B, w.H, w.Hkv, w.N, w.d, causal=True)
-    say(f"  {w.name}: {rows16}-row waves")
-    if torch.cuda.get_device_properties(0).multi_processor_count >= 128:
-        assert rows16 == 16
+    groups = binding.fwd_walk_groups(w.B, w.H, w.Hkv, w.N, w.d, causal=True)
+    say(f"  {w.name}: {groups} walk group(s)")
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 171:
+        assert groups == 2
     inp, t, o, c = _run(w, "reverse", 256.0, heads=[(0, 0), (0, 3)], n_rows=320)
     assert _presink_fraction_ok(c, w)
     one = {k: v[0:1, 2:3].contiguous() for k, v in t.items()}
