@@ -8,7 +8,9 @@
 // Layout of the work on the chip
 // ------------------------------
 // * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32
-//   rows. K/V blocks of 64 keys stream through LDS (two stages, double-buffered).
+//   rows. K/V blocks of 64 keys stream through LDS (two stages, double-buffered). Small
+//   d = 128 grids run fwd_pair_kernel instead: 64 rows per workgroup, whose KV walk two
+//   groups of two waves split (fwd_body, NG = 2).
 // * Both GEMMs use v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32). That instruction
 //   truncates small products inside its adder tree; the exact-Q.K^T variant (QX) forms
 //   S^T on v_mfma_f32_32x32x16_bf16 instead, from keys converted once to bf16 and queries
